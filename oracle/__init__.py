@@ -1,0 +1,149 @@
+"""Python handle on the fp64 Engram gate oracle (``engram_oracle.cpp``).
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, by ``__graft_entry__.smoke()``
+and by the CPU-baseline leg of ``bench.py``.  The GPU library never imports,
+links or calls it, and it imports nothing from the GPU library.
+
+What it computes is the gate of the zhichai.net TileKernels page, section
+"5. Engram" (gate formula), and its chain-rule backward; the readings taken
+where that page is silent are listed at the top of ``engram_oracle.cpp``.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "engram_oracle.cpp")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+EPS = 1e-6          # RMSNorm epsilon used throughout (the pages give none)
+CLAMP = 1e-4        # lower clamp of |z| in the signed-sqrt derivative
+
+
+def build(verbose: bool = False) -> str:
+    """Compile the oracle with g++ (no fast-math, no FMA contraction)."""
+    cmd = ["g++", "-O2", "-std=c++17", "-ffp-contract=off", "-fPIC", "-shared",
+           "-pthread", _SRC, "-o", _LIB]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.run(cmd, check=True)
+    return _LIB
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            raise RuntimeError(f"{_LIB} is missing: run __graft_entry__.build()")
+        L = ctypes.CDLL(_LIB)
+        vp, i64, dbl, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_double, ctypes.c_int
+        L.oracle_fwd_f64.argtypes = [vp, vp, vp, vp, vp, i64, i64, dbl, vp, vp, vp]
+        L.oracle_bwd_f64.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, dbl, dbl,
+                                     vp, vp, vp, vp, vp, vp]
+        L.oracle_fwd_bf16.argtypes = [vp, vp, vp, vp, vp, i64, i64, dbl, vp, vp, vp, i32]
+        L.oracle_bwd_bf16.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, dbl, dbl,
+                                      vp, vp, vp, vp, vp, vp, i32]
+        L.oracle_round_bf16.argtypes = [vp, i64, vp]
+        for n in ("oracle_fwd_f64", "oracle_bwd_f64", "oracle_fwd_bf16",
+                  "oracle_bwd_bf16", "oracle_round_bf16"):
+            getattr(L, n).restype = None
+        L.oracle_fwd_stats_width.restype = i32
+        L.oracle_bwd_stats_width.restype = i32
+        _lib = L
+    return _lib
+
+
+def _p(a):
+    if a is None:
+        return None
+    assert isinstance(a, np.ndarray) and a.flags["C_CONTIGUOUS"], "need C-contiguous"
+    return a.ctypes.data
+
+
+def _f64(a):
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def default_threads() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+# ---- fp64 inputs ------------------------------------------------------------
+
+def fwd_f64(x, k, v, wh, we, eps=EPS):
+    """Forward on fp64 arrays.  Returns (out [T,H], gate [T], stats [T,8]) with
+    stats columns mean(x^2), mean(k^2), r_x, r_k, d, z, s, gate."""
+    x, k, v, wh, we = map(_f64, (x, k, v, wh, we))
+    T, H = x.shape
+    out = np.empty((T, H)); gate = np.empty(T); st = np.empty((T, 8))
+    lib().oracle_fwd_f64(_p(x), _p(k), _p(v), _p(wh), _p(we), T, H, eps,
+                         _p(out), _p(gate), _p(st))
+    return out, gate, st
+
+
+def bwd_f64(gout, x, k, v, wh, we, eps=EPS, clamp=CLAMP):
+    """Backward on fp64 arrays.  Returns (dx, dk, dv, dwh, dwe, stats [T,4])
+    with stats columns dgate, ds, dz, dd."""
+    gout, x, k, v, wh, we = map(_f64, (gout, x, k, v, wh, we))
+    T, H = x.shape
+    dx = np.empty((T, H)); dk = np.empty((T, H)); dv = np.empty((T, H))
+    dwh = np.empty(H); dwe = np.empty(H); st = np.empty((T, 4))
+    lib().oracle_bwd_f64(_p(gout), _p(x), _p(k), _p(v), _p(wh), _p(we), T, H, eps,
+                         clamp, _p(dx), _p(dk), _p(dv), _p(dwh), _p(dwe), _p(st))
+    return dx, dk, dv, dwh, dwe, st
+
+
+# ---- bf16 inputs (uint16 bit patterns), multithreaded -------------------------
+
+def fwd_bf16(x, k, v, wh, we, eps=EPS, want_out=True, threads=None):
+    """Forward over bf16 rows.  Returns (out fp64 [rows,H] or None, gate, z)."""
+    rows, H = x.shape
+    for a in (x, k, v):
+        assert a.dtype == np.uint16 and a.shape == (rows, H) and a.flags["C_CONTIGUOUS"]
+    wh = np.ascontiguousarray(wh, dtype=np.float32)
+    we = np.ascontiguousarray(we, dtype=np.float32)
+    out = np.empty((rows, H)) if want_out else None
+    gate = np.empty(rows); z = np.empty(rows)
+    lib().oracle_fwd_bf16(_p(x), _p(k), _p(v), _p(wh), _p(we), rows, H, eps,
+                          _p(out), _p(gate), _p(z), threads or default_threads())
+    return out, gate, z
+
+
+def bwd_bf16(gout, x, k, v, wh, we, eps=EPS, clamp=CLAMP, want_grads=True,
+             threads=None):
+    """Backward over bf16 rows.  Returns (dx, dk, dv or Nones, dwh, dwe, dd)."""
+    rows, H = x.shape
+    for a in (gout, x, k, v):
+        assert a.dtype == np.uint16 and a.shape == (rows, H) and a.flags["C_CONTIGUOUS"]
+    wh = np.ascontiguousarray(wh, dtype=np.float32)
+    we = np.ascontiguousarray(we, dtype=np.float32)
+    if want_grads:
+        dx = np.empty((rows, H)); dk = np.empty((rows, H)); dv = np.empty((rows, H))
+    else:
+        dx = dk = dv = None
+    dwh = np.empty(H); dwe = np.empty(H); dd = np.empty(rows)
+    lib().oracle_bwd_bf16(_p(gout), _p(x), _p(k), _p(v), _p(wh), _p(we), rows, H,
+                          eps, clamp, _p(dx), _p(dk), _p(dv), _p(dwh), _p(dwe),
+                          _p(dd), threads or default_threads())
+    return dx, dk, dv, dwh, dwe, dd
+
+
+def round_bf16(a) -> np.ndarray:
+    """fp64 -> bf16 bit patterns, nearest-even."""
+    a = _f64(a)
+    out = np.empty(a.shape, dtype=np.uint16)
+    lib().oracle_round_bf16(_p(a), a.size, _p(out))
+    return out
+
+
+def bf16_to_f64(bits) -> np.ndarray:
+    bits = np.asarray(bits, dtype=np.uint16)
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)

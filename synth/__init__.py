@@ -1,0 +1,217 @@
+"""Seeded synthetic inputs for the Engram gate workloads.
+
+The gate itself is described on the zhichai.net TileKernels page, section
+"5. Engram" (gate formula): per token a hidden row x, a key row k and a value
+row v, all of width H, plus two per-channel RMSNorm weights wh and we.  The
+pages print no data, so every workload here is drawn from a counter-based
+generator (Philox-4x32-10) with a fixed seed, with the shapes of the pages'
+example ([batch, seq_len, hidden_dim] with hidden_dim in {4096, 7168}).
+
+This module holds none of the gate's arithmetic.  It produces host arrays:
+bf16 tensors as uint16 bit patterns, fp32 weights as float32.  Both the fp64
+oracle (``oracle/``) and the GPU library consume the identical bytes.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from dataclasses import dataclass
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "synth.cpp")
+_LIB = os.path.join(_HERE, "libsynth.so")
+
+# Stream ids: one independent Philox stream per tensor or per-row draw.
+STREAM_X, STREAM_K, STREAM_V, STREAM_GOUT = 1, 2, 3, 4
+STREAM_WH, STREAM_WE = 5, 6
+STREAM_RHO, STREAM_KNOISE = 7, 8
+STREAM_MASK = {"x": 9, "k": 10, "v": 11}
+
+
+def build(verbose: bool = False) -> str:
+    """Compile the generator with g++ into ``synth/libsynth.so``."""
+    cmd = ["g++", "-O2", "-std=c++17", "-fPIC", "-shared", "-pthread",
+           _SRC, "-o", _LIB]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.run(cmd, check=True)
+    return _LIB
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            raise RuntimeError(f"{_LIB} is missing: run __graft_entry__.build()")
+        L = ctypes.CDLL(_LIB)
+        u64, u32, i64, i32, dbl = (ctypes.c_uint64, ctypes.c_uint32,
+                                   ctypes.c_int64, ctypes.c_int, ctypes.c_double)
+        vp = ctypes.c_void_p
+        L.synth_philox4x32_10.argtypes = [vp, vp, vp]
+        L.synth_round_bf16.argtypes = [vp, i64, vp]
+        L.synth_normal_bf16.argtypes = [u64, u32, i64, i64, dbl, vp, i32]
+        L.synth_normal_f32.argtypes = [u64, u32, i64, i64, dbl, dbl, vp]
+        L.synth_uniform_pm1.argtypes = [u64, u32, i64, i64, vp]
+        L.synth_row_keys.argtypes = [u64, u32, i64, vp]
+        L.synth_correlated_bf16.argtypes = [u64, u32, vp, vp, i64, i64, i64, vp, i32]
+        L.synth_student_t3_bf16.argtypes = [u64, u32, i64, i64, i64, vp, vp, i32]
+        for name in ("synth_philox4x32_10", "synth_round_bf16", "synth_normal_bf16",
+                     "synth_normal_f32", "synth_uniform_pm1", "synth_row_keys",
+                     "synth_correlated_bf16", "synth_student_t3_bf16"):
+            getattr(L, name).restype = None
+        _lib = L
+    return _lib
+
+
+def default_threads() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def _p(a: np.ndarray) -> int:
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data
+
+
+# ---- primitive draws -------------------------------------------------------
+
+def philox4x32_10(ctr, key) -> np.ndarray:
+    c = np.asarray(ctr, dtype=np.uint32)
+    k = np.asarray(key, dtype=np.uint32)
+    out = np.zeros(4, dtype=np.uint32)
+    lib().synth_philox4x32_10(_p(c), _p(k), _p(out))
+    return out
+
+
+def round_bf16(v: np.ndarray) -> np.ndarray:
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    out = np.empty(v.shape, dtype=np.uint16)
+    lib().synth_round_bf16(_p(v), v.size, _p(out))
+    return out
+
+
+def normal_bf16(seed, stream, shape, e0=0, scale=1.0, threads=None) -> np.ndarray:
+    out = np.empty(shape, dtype=np.uint16)
+    lib().synth_normal_bf16(seed, stream, e0, out.size, scale, _p(out),
+                            threads or default_threads())
+    return out
+
+
+def normal_f32(seed, stream, n, mean=0.0, std=1.0) -> np.ndarray:
+    out = np.empty(n, dtype=np.float32)
+    lib().synth_normal_f32(seed, stream, 0, n, mean, std, _p(out))
+    return out
+
+
+def uniform_pm1(seed, stream, n, e0=0) -> np.ndarray:
+    out = np.empty(n, dtype=np.float64)
+    lib().synth_uniform_pm1(seed, stream, e0, n, _p(out))
+    return out
+
+
+def row_keys(seed, stream, n) -> np.ndarray:
+    out = np.empty(n, dtype=np.uint64)
+    lib().synth_row_keys(seed, stream, n, _p(out))
+    return out
+
+
+def correlated_bf16(seed, x_bits, rho, t0=0, threads=None) -> np.ndarray:
+    rows, H = x_bits.shape
+    out = np.empty_like(x_bits)
+    lib().synth_correlated_bf16(seed, STREAM_KNOISE, _p(x_bits), _p(rho), t0, rows,
+                                H, _p(out), threads or default_threads())
+    return out
+
+
+def student_t3_bf16(seed, stream, rows, H, row_scale, t0=0, threads=None) -> np.ndarray:
+    row_scale = np.ascontiguousarray(row_scale, dtype=np.float64)
+    assert row_scale.shape == (rows,)
+    out = np.empty((rows, H), dtype=np.uint16)
+    lib().synth_student_t3_bf16(seed, stream, t0, rows, H, _p(row_scale), _p(out),
+                                threads or default_threads())
+    return out
+
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact widening of bf16 bit patterns (for test-side statistics only)."""
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+# ---- the five workloads ----------------------------------------------------
+
+@dataclass(frozen=True)
+class Config:
+    name: str
+    T: int
+    H: int
+    kind: str          # "normal", "correlated" or "stress"
+    fwd_only: bool
+    describe: str
+
+
+CONFIGS = {
+    1: Config("tiny", 64, 256, "normal", False,
+              "T=64 tokens, H=256, x,k,v ~ N(0,1) bf16, wh,we = 1+0.1N(0,1) fp32, "
+              "grad_out ~ N(0,1), eps=1e-6, seed 0"),
+    2: Config("fwd_b2s512_h4096", 2 * 512, 4096, "normal", True,
+              "forward only, batch 2 x seq 512 = 1024 tokens, H=4096, x,k,v ~ N(0,1)"),
+    3: Config("fwdbwd_b4s4096_h4096", 4 * 4096, 4096, "correlated", False,
+              "fwd+bwd, batch 4 x seq 4096 = 16384 tokens, H=4096, x,v ~ N(0,1), "
+              "k = rho x + sqrt(1-rho^2) N(0,1), rho ~ U[-1,1] per token"),
+    4: Config("fwdbwd_b8s4096_h7168", 8 * 4096, 7168, "correlated", False,
+              "fwd+bwd, batch 8 x seq 4096 = 32768 tokens, H=7168, correlated k"),
+    5: Config("stress_t65537_h7168", 65537, 7168, "stress", False,
+              "stress fwd+bwd, T=65537 (ragged), H=7168, x,k,v ~ Student-t(3), "
+              "0.1% rows x1e3 and 0.1% rows all-zero per tensor"),
+}
+
+
+def stress_row_scales(seed: int, T: int, tensor: str) -> np.ndarray:
+    """Per-row scale for a stress tensor: 1, 1e3 (round(0.001 T) rows) or 0
+    (another round(0.001 T) rows, disjoint), rows picked by sorting Philox keys."""
+    n = int(round(0.001 * T))
+    order = np.argsort(row_keys(seed, STREAM_MASK[tensor], T), kind="stable")
+    s = np.ones(T, dtype=np.float64)
+    s[order[:n]] = 1e3
+    s[order[n:2 * n]] = 0.0
+    return s
+
+
+def make_inputs(cfg: int | Config, seed: int = 0, rows: tuple[int, int] | None = None,
+                threads: int | None = None, with_grad: bool = True) -> dict:
+    """Host arrays for a workload, optionally only rows [r0, r1) of it.
+
+    Returns x, k, v (and grad_out) as uint16 bf16 bits of shape [rows, H],
+    wh and we as float32 [H], plus T, H and r0."""
+    c = CONFIGS[cfg] if isinstance(cfg, int) else cfg
+    T, H = c.T, c.H
+    r0, r1 = rows if rows is not None else (0, T)
+    assert 0 <= r0 <= r1 <= T
+    n = r1 - r0
+    e0 = r0 * H
+    th = threads or default_threads()
+    out = {"T": T, "H": H, "r0": r0, "config": c}
+    out["wh"] = normal_f32(seed, STREAM_WH, H, 1.0, 0.1)
+    out["we"] = normal_f32(seed, STREAM_WE, H, 1.0, 0.1)
+    if c.kind == "stress":
+        for name, stream in (("x", STREAM_X), ("k", STREAM_K), ("v", STREAM_V)):
+            s = stress_row_scales(seed, T, name)[r0:r1]
+            out[name] = student_t3_bf16(seed, stream, n, H, s, t0=r0, threads=th)
+    else:
+        out["x"] = normal_bf16(seed, STREAM_X, (n, H), e0=e0, threads=th)
+        out["v"] = normal_bf16(seed, STREAM_V, (n, H), e0=e0, threads=th)
+        if c.kind == "correlated":
+            rho = uniform_pm1(seed, STREAM_RHO, n, e0=r0)
+            out["rho"] = rho
+            out["k"] = correlated_bf16(seed, out["x"], rho, t0=r0, threads=th)
+        else:
+            out["k"] = normal_bf16(seed, STREAM_K, (n, H), e0=e0, threads=th)
+    if with_grad:
+        out["grad_out"] = normal_bf16(seed, STREAM_GOUT, (n, H), e0=e0, threads=th)
+    return out
