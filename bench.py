@@ -1,0 +1,275 @@
+"""Benchmark of the Engram gate on one MI355X.
+
+One step = one pass of the whole path over one batch of tokens:
+tk_engram_gate_fwd, then tk_engram_gate_bwd, then tk_engram_grad_w_reduce,
+all on the same stream, inputs already resident in HBM.
+
+Prints one JSON line: fwd+bwd tokens/s on the main workload, the roofline of
+the dominant kernel (HBM-bound; algorithmic bytes / average launch time from
+HIP events on the launch stream against 8 TB/s), the same figures for the
+other tuned width, a plain 128-bit copy as the practical HBM ceiling, and the
+fp64 oracle's throughput on the host as a reported CPU baseline.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 4]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+HBM_PEAK_GBPS = 8000.0          # MI355X published HBM3E bandwidth
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SRC = os.path.join(ROOT, "engram_conditional_memory_amd", "csrc", "engram_gate.hip")
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def algorithmic_bytes(T: int, H: int) -> dict:
+    """Bytes the method itself must move per launch (bf16 tensors, fp32 [H]
+    weights and the fp32 gate); partial sums are implementation overhead."""
+    return {
+        "fwd": 8 * T * H + 4 * T + 8 * H,        # read x, k, v; write out, gate
+        "bwd": 14 * T * H + 8 * H,               # read g, x, k, v; write dx, dk, dv
+    }
+
+
+def to_dev(bits, dev):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+
+class Workload:
+    def __init__(self, cfg: int, dev, eg):
+        import synth
+        import torch
+        c = synth.CONFIGS[cfg]
+        self.cfg, self.c, self.T, self.H = cfg, c, c.T, c.H
+        d = synth.make_inputs(cfg)
+        self.host = d
+        self.x, self.k, self.v = to_dev(d["x"], dev), to_dev(d["k"], dev), to_dev(d["v"], dev)
+        self.g = to_dev(d["grad_out"], dev)
+        self.wh = torch.from_numpy(d["wh"]).to(dev)
+        self.we = torch.from_numpy(d["we"]).to(dev)
+        T, H = self.T, self.H
+        bf = torch.bfloat16
+        self.out = torch.empty((T, H), dtype=bf, device=dev)
+        self.gate = torch.empty((T,), dtype=torch.float32, device=dev)
+        self.dx = torch.empty((T, H), dtype=bf, device=dev)
+        self.dk = torch.empty((T, H), dtype=bf, device=dev)
+        self.dv = torch.empty((T, H), dtype=bf, device=dev)
+        self.P = eg.tk_engram_num_partials(T, H)
+        self.ws = torch.empty((max(1, self.P), H), dtype=torch.float32, device=dev)
+        self.dwh = torch.empty((H,), dtype=torch.float32, device=dev)
+        self.dwe = torch.empty((H,), dtype=torch.float32, device=dev)
+        self.eg = eg
+
+    def step(self, ev=None):
+        eg = self.eg
+        if ev is not None:
+            ev[0].record()
+        eg.tk_engram_gate_fwd(self.x, self.k, self.v, self.wh, self.we, self.out, self.gate)
+        if ev is not None:
+            ev[1].record()
+        eg.tk_engram_gate_bwd(self.g, self.x, self.k, self.v, self.wh, self.we,
+                              self.dx, self.dk, self.dv, self.ws)
+        if ev is not None:
+            ev[2].record()
+        eg.tk_engram_grad_w_reduce(self.ws, self.P, self.H, self.wh, self.we,
+                                   self.dwh, self.dwe)
+        if ev is not None:
+            ev[3].record()
+
+    def free(self):
+        for n in ("x", "k", "v", "g", "out", "gate", "dx", "dk", "dv", "ws", "dwh", "dwe"):
+            setattr(self, n, None)
+
+
+def time_workload(w: Workload, steps: int, warmup: int) -> dict:
+    import torch
+    for _ in range(warmup):
+        w.step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(steps):
+        w.step(evs[i])
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(stop)
+    fwd = [e[0].elapsed_time(e[1]) for e in evs]
+    bwd = [e[1].elapsed_time(e[2]) for e in evs]
+    red = [e[2].elapsed_time(e[3]) for e in evs]
+    T, H = w.T, w.H
+    ab = algorithmic_bytes(T, H)
+    ms_step = total_ms / steps
+    f_us, b_us, r_us = (1e3 * float(np.mean(a)) for a in (fwd, bwd, red))
+    res = {
+        "workload": w.c.name, "T": T, "H": H, "P": w.P,
+        "ms_per_step": ms_step, "wall_s": wall,
+        "tokens_per_s": T / (ms_step / 1e3),
+        "fwd": {"us": f_us, "us_median": 1e3 * float(np.median(fwd)),
+                "tokens_per_s": T / (f_us / 1e6), "bytes": ab["fwd"],
+                "GBps": ab["fwd"] / (f_us * 1e3), "frac": ab["fwd"] / (f_us * 1e3) / HBM_PEAK_GBPS},
+        "bwd_kernel": {"us": b_us, "us_median": 1e3 * float(np.median(bwd)), "bytes": ab["bwd"],
+                       "GBps": ab["bwd"] / (b_us * 1e3),
+                       "frac": ab["bwd"] / (b_us * 1e3) / HBM_PEAK_GBPS},
+        "reduce_us": r_us,
+        "bwd": {"us": b_us + r_us, "tokens_per_s": T / ((b_us + r_us) / 1e6),
+                "GBps": ab["bwd"] / ((b_us + r_us) * 1e3),
+                "frac": ab["bwd"] / ((b_us + r_us) * 1e3) / HBM_PEAK_GBPS},
+    }
+    return res
+
+
+def copy_ceiling(nbytes: int, eg, dev, reps: int = 20) -> dict:
+    import torch
+    src = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        eg.tk_engram_copy_probe(src, dst)
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        eg.tk_engram_copy_probe(src, dst)
+    b.record()
+    torch.cuda.synchronize()
+    us = 1e3 * a.elapsed_time(b) / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"bytes_moved": 2 * nbytes, "us": us, "GBps": 2 * nbytes / (us * 1e3),
+            "frac": 2 * nbytes / (us * 1e3) / HBM_PEAK_GBPS}
+
+
+def cpu_baseline(host: dict) -> dict:
+    """The fp64 oracle, as it stands, on the host cores: forward + backward
+    over every token of the workload once."""
+    import oracle
+    th = oracle.default_threads()
+    T = host["x"].shape[0]
+    t0 = time.perf_counter()
+    oracle.fwd_bf16(host["x"], host["k"], host["v"], host["wh"], host["we"],
+                    want_out=True, threads=th)
+    oracle.bwd_bf16(host["grad_out"], host["x"], host["k"], host["v"], host["wh"],
+                    host["we"], threads=th)
+    dt = time.perf_counter() - t0
+    return {"value": T / dt, "unit": "tokens/s", "cores": th, "kind": "oracle",
+            "sample": f"all {T} tokens of the workload, fp64 forward + backward "
+                      f"(incl. dwh/dwe), one pass, {dt:.2f} s wall"}
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel source; else None."""
+    path = os.path.join(PROFILES, f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=4, choices=[3, 4, 5],
+                    help="main workload (3: T=16384 H=4096, 4: T=32768 H=7168, 5: stress)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the second tuned width")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not "
+              "supported (the path shards by tokens; see the design notes).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import engram_conditional_memory_amd as eg
+    eg.load_library()
+    dev = torch.device("cuda:0")
+
+    print(f"[bench] generating workload {args.workload}", file=sys.stderr, flush=True)
+    w = Workload(args.workload, dev, eg)
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    main_res = time_workload(w, args.steps, args.warmup)
+    host = w.host
+    w.free()
+    torch.cuda.empty_cache()
+
+    secondary = None
+    if not args.no_secondary:
+        other = 3 if args.workload != 3 else 4
+        print(f"[bench] generating workload {other}", file=sys.stderr, flush=True)
+        w2 = Workload(other, dev, eg)
+        secondary = time_workload(w2, args.steps, args.warmup)
+        w2.free()
+        del w2
+        torch.cuda.empty_cache()
+
+    copy = copy_ceiling(2 * main_res["T"] * main_res["H"], eg, dev)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(host)
+
+    bk = main_res["bwd_kernel"]
+    traffic = measured_traffic("gate_bwd_kernel", main_res["workload"])
+    line = {
+        "metric": "Engram gate fwd+bwd tokens/s and achieved HBM GB/s, bf16 H=4096/7168",
+        "value": main_res["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": main_res["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded Philox-4x32-10 inputs of the stated recipe)",
+        "config": {"workload": main_res["workload"], "tokens": main_res["T"],
+                   "hidden": main_res["H"], "tensor_dtype": "bf16",
+                   "step": "gate_fwd + gate_bwd + grad_w_reduce", "partials": main_res["P"]},
+        "roofline": {"bound": "hbm", "kernel": "gate_bwd_kernel",
+                     "achieved": bk["GBps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": bk["frac"], "traffic": traffic},
+        "fwd": main_res["fwd"],
+        "bwd": main_res["bwd"],
+        "bwd_kernel": bk,
+        "reduce_us": main_res["reduce_us"],
+        "secondary": secondary,
+        "copy_probe": copy,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,26 @@
+"""Engram gate for AMD MI355X: Python binding of the HIP library libtk_engram.so.
+
+The gate (zhichai.net TileKernels page, section "5. Engram", gate formula):
+    gate = sigmoid(signed_sqrt(dot(RMSNorm(x, wh), RMSNorm(k, we)) / sqrt(H)))
+    out  = x + gate * v
+with its backward (dx, dk, dv) and the weight-gradient reduction (dwh, dwe).
+The C ABI is declared in include/tk_engram.h; the functions below have the
+same names and only marshal torch tensors into it.
+"""
+
+from ._binding import (  # noqa: F401
+    DSQRT_CLAMP,
+    EPS,
+    EXPORTS,
+    TkError,
+    load_library,
+    tk_abi_version,
+    tk_engram_bwd_workspace_bytes,
+    tk_engram_copy_probe,
+    tk_engram_gate_bwd,
+    tk_engram_gate_fwd,
+    tk_engram_grad_w_reduce,
+    tk_engram_num_partials,
+    tk_status_string,
+)
+from .build import LIB as LIBRARY_PATH  # noqa: F401

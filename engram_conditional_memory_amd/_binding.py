@@ -1,0 +1,214 @@
+"""ctypes binding of libtk_engram.so (declared in include/tk_engram.h).
+
+Argument marshalling only: tensors are checked for dtype, shape, device and
+contiguity, their device pointers and the current HIP stream are passed to
+the C ABI, and a nonzero status raises.  Every step of the gate runs in the
+library's HIP kernels; there is no other implementation to fall back to, and
+a missing library raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+from .build import LIB
+
+EPS = 1e-6            # RMSNorm epsilon
+DSQRT_CLAMP = 1e-4    # lower clamp of |z| in the signed-sqrt derivative
+
+TK_SUCCESS = 0
+TK_ERR_NULL = 1
+TK_ERR_SHAPE = 2
+TK_ERR_ALIGN = 3
+TK_ERR_UNSUPPORTED = 4
+TK_ERR_WORKSPACE = 5
+TK_ERR_LAUNCH = 6
+TK_ERR_VALUE = 7
+
+EXPORTS = (
+    "tk_engram_gate_fwd", "tk_engram_gate_bwd", "tk_engram_grad_w_reduce",
+    "tk_engram_num_partials", "tk_engram_bwd_workspace_bytes",
+    "tk_engram_copy_probe", "tk_status_string", "tk_abi_version",
+)
+
+
+class TkError(RuntimeError):
+    def __init__(self, call: str, status: int, message: str):
+        super().__init__(f"{call}: {message} (status {status})")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: str = LIB) -> ctypes.CDLL:
+    """Load the library once; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with __graft_entry__.build() "
+            "(the Engram gate has no implementation other than its HIP kernels)")
+    L = ctypes.CDLL(path)
+    vp, i64, sz, dbl, i32 = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t,
+                             ctypes.c_double, ctypes.c_int32)
+    L.tk_engram_gate_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, dbl, vp]
+    L.tk_engram_gate_fwd.restype = i32
+    L.tk_engram_gate_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
+                                     i64, i64, dbl, dbl, vp]
+    L.tk_engram_gate_bwd.restype = i32
+    L.tk_engram_grad_w_reduce.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp]
+    L.tk_engram_grad_w_reduce.restype = i32
+    L.tk_engram_num_partials.argtypes = [i64, i64]
+    L.tk_engram_num_partials.restype = i64
+    L.tk_engram_bwd_workspace_bytes.argtypes = [i64, i64]
+    L.tk_engram_bwd_workspace_bytes.restype = sz
+    L.tk_engram_copy_probe.argtypes = [vp, vp, sz, vp]
+    L.tk_engram_copy_probe.restype = i32
+    L.tk_status_string.argtypes = [i32]
+    L.tk_status_string.restype = ctypes.c_char_p
+    L.tk_abi_version.argtypes = []
+    L.tk_abi_version.restype = i32
+    _lib = L
+    return L
+
+
+def tk_status_string(status: int) -> str:
+    return load_library().tk_status_string(status).decode()
+
+
+def tk_abi_version() -> int:
+    return int(load_library().tk_abi_version())
+
+
+def tk_engram_num_partials(T: int, H: int) -> int:
+    return int(load_library().tk_engram_num_partials(T, H))
+
+
+def tk_engram_bwd_workspace_bytes(T: int, H: int) -> int:
+    return int(load_library().tk_engram_bwd_workspace_bytes(T, H))
+
+
+def _check(call: str, status: int) -> None:
+    if status != TK_SUCCESS:
+        raise TkError(call, status, tk_status_string(status))
+
+
+# ---- tensor marshalling ----------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_handle(device, stream):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t, name, dtype, shape, device):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _rows(x, name="x"):
+    torch = _torch()
+    if not isinstance(x, torch.Tensor) or x.dim() != 2:
+        raise ValueError(f"{name} must be a 2-D [T, H] tensor")
+    if x.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor")
+    return x.shape[0], x.shape[1], x.device
+
+
+def tk_engram_gate_fwd(x, k, v, wh, we, out=None, gate=None, eps=EPS, stream=None):
+    """out = x + gate * v and gate [T] (fp32); x, k, v bf16 [T, H]."""
+    torch = _torch()
+    T, H, dev = _rows(x)
+    bf, f32 = torch.bfloat16, torch.float32
+    if out is None:
+        out = torch.empty((T, H), dtype=bf, device=dev)
+    if gate is None:
+        gate = torch.empty((T,), dtype=f32, device=dev)
+    args = [_need(x, "x", bf, (T, H), dev), _need(k, "k", bf, (T, H), dev),
+            _need(v, "v", bf, (T, H), dev), _need(wh, "wh", f32, (H,), dev),
+            _need(we, "we", f32, (H,), dev), _need(out, "out", bf, (T, H), dev),
+            _need(gate, "gate", f32, (T,), dev)]
+    st = load_library().tk_engram_gate_fwd(*args, T, H, float(eps),
+                                           _stream_handle(dev, stream))
+    _check("tk_engram_gate_fwd", st)
+    return out, gate
+
+
+def tk_engram_gate_bwd(grad_out, x, k, v, wh, we, dx=None, dk=None, dv=None,
+                       workspace=None, eps=EPS, dsqrt_clamp=DSQRT_CLAMP, stream=None):
+    """dx, dk, dv (bf16 [T, H]) and the fp32 [P, H] weight-gradient partials."""
+    torch = _torch()
+    T, H, dev = _rows(x)
+    bf, f32 = torch.bfloat16, torch.float32
+    P = tk_engram_num_partials(T, H)
+    if dx is None:
+        dx = torch.empty((T, H), dtype=bf, device=dev)
+    if dk is None:
+        dk = torch.empty((T, H), dtype=bf, device=dev)
+    if dv is None:
+        dv = torch.empty((T, H), dtype=bf, device=dev)
+    if workspace is None:
+        workspace = torch.empty((max(P, 1), H), dtype=f32, device=dev)
+    if workspace.dtype != f32 or workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous fp32 GPU tensor")
+    args = [_need(grad_out, "grad_out", bf, (T, H), dev), _need(x, "x", bf, (T, H), dev),
+            _need(k, "k", bf, (T, H), dev), _need(v, "v", bf, (T, H), dev),
+            _need(wh, "wh", f32, (H,), dev), _need(we, "we", f32, (H,), dev),
+            _need(dx, "dx", bf, (T, H), dev), _need(dk, "dk", bf, (T, H), dev),
+            _need(dv, "dv", bf, (T, H), dev), ctypes.c_void_p(workspace.data_ptr())]
+    st = load_library().tk_engram_gate_bwd(*args, workspace.numel() * 4, T, H,
+                                           float(eps), float(dsqrt_clamp),
+                                           _stream_handle(dev, stream))
+    _check("tk_engram_gate_bwd", st)
+    return dx, dk, dv, workspace, P
+
+
+def tk_engram_grad_w_reduce(workspace, P, H, wh, we, dwh=None, dwe=None, stream=None):
+    """dwh = we * sum_p workspace[p], dwe = wh * sum_p workspace[p] (fp32 [H])."""
+    torch = _torch()
+    dev = wh.device
+    f32 = torch.float32
+    if workspace.dtype != f32 or workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous fp32 tensor on wh's device")
+    if workspace.numel() < P * H:
+        raise ValueError("workspace holds fewer than P * H values")
+    if dwh is None:
+        dwh = torch.empty((H,), dtype=f32, device=dev)
+    if dwe is None:
+        dwe = torch.empty((H,), dtype=f32, device=dev)
+    st = load_library().tk_engram_grad_w_reduce(
+        ctypes.c_void_p(workspace.data_ptr()), P, H, _need(wh, "wh", f32, (H,), dev),
+        _need(we, "we", f32, (H,), dev), _need(dwh, "dwh", f32, (H,), dev),
+        _need(dwe, "dwe", f32, (H,), dev), _stream_handle(dev, stream))
+    _check("tk_engram_grad_w_reduce", st)
+    return dwh, dwe
+
+
+def tk_engram_copy_probe(src, dst, stream=None):
+    """Copy src into dst (same byte size) with the library's 128-bit copy."""
+    n = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != n:
+        raise ValueError("src and dst differ in size")
+    st = load_library().tk_engram_copy_probe(ctypes.c_void_p(src.data_ptr()),
+                                             ctypes.c_void_p(dst.data_ptr()), n,
+                                             _stream_handle(src.device, stream))
+    _check("tk_engram_copy_probe", st)
+    return dst

@@ -1,0 +1,161 @@
+/*
+ * tk_engram.h — C ABI of the Engram gate library for AMD MI355X (gfx950).
+ *
+ * The operation is the Engram gate of DeepSeek's TileKernels as described on
+ * the zhichai.net TileKernels page, section "5. Engram" (gate formula). Per
+ * token (row) t, with x the hidden row (the formula's hidden_states), k the
+ * key row, v the value row, all of width H, and per-channel RMSNorm weights
+ * wh and we:
+ *
+ *   r_x    = 1 / sqrt(mean(x^2) + eps)      RMSNorm(x, wh) = x * r_x * wh
+ *   r_k    = 1 / sqrt(mean(k^2) + eps)      RMSNorm(k, we) = k * r_k * we
+ *   d      = dot(RMSNorm(x, wh), RMSNorm(k, we))
+ *   z      = d / sqrt(H)                    (the formula's scalar)
+ *   gate   = sigmoid(sign(z) * sqrt(|z|))   (signed_sqrt, then sigmoid)
+ *   out    = x + gate * v
+ *
+ * The same section splits the work into a fused forward, its backward and a
+ * separate weight-gradient reduction; the juejin.cn page (highlight 5) says
+ * the PyTorch binding covers forward, backward and weight-gradient
+ * reduction. The three calls below are that split.
+ *
+ * Conventions shared by every call:
+ *   - Tensors are row-major and contiguous. bf16 tensors cross the ABI as
+ *     uint16_t bit patterns; [T, H] means row stride H elements.
+ *   - All pointers are DEVICE pointers owned by the caller. The library
+ *     never allocates, frees or synchronises; each call only enqueues work
+ *     on `stream` (a hipStream_t passed as void*, NULL = default stream)
+ *     and returns. Outputs are overwritten, never accumulated into.
+ *   - Inputs and outputs must not overlap (undefined behaviour otherwise).
+ *   - Arithmetic: fp32 elementwise work with fp32 sums, except the weighted
+ *     dot product sum_i x_i k_i wh_i we_i, which is accumulated in fp64 so
+ *     that the gate stays accurate where the dot product is near zero.
+ *     bf16 results are rounded to nearest, ties to even.
+ *   - Every call is deterministic: the row-to-workgroup assignment depends
+ *     only on (T, H), and no atomics are used, so reruns are bit-identical.
+ *   - Errors: arguments are checked before any device work; a failed check
+ *     returns its status and enqueues nothing. A launch failure returns
+ *     TK_ERR_LAUNCH. Faults inside kernels surface at the caller's next
+ *     synchronisation, as for any HIP kernel.
+ *   - Shape limits: 0 <= T, 8 <= H <= 8192, H a multiple of 8; T = 0 is a
+ *     successful no-op for the forward and backward.
+ *   - Alignment: every tensor pointer must be 16-byte aligned (128-bit
+ *     loads and stores), except `gate` which needs 4 bytes.
+ */
+#ifndef TK_ENGRAM_H
+#define TK_ENGRAM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t tk_status;
+
+enum {
+  TK_SUCCESS = 0,
+  TK_ERR_NULL = 1,        /* a required pointer is NULL                     */
+  TK_ERR_SHAPE = 2,       /* T < 0, H <= 0, or P inconsistent               */
+  TK_ERR_ALIGN = 3,       /* H not a multiple of 8 or a pointer misaligned  */
+  TK_ERR_UNSUPPORTED = 4, /* H above the supported maximum                  */
+  TK_ERR_WORKSPACE = 5,   /* backward workspace smaller than required       */
+  TK_ERR_LAUNCH = 6,      /* the HIP runtime refused the kernel launch      */
+  TK_ERR_VALUE = 7        /* eps or clamp not a finite positive number      */
+};
+
+#define TK_ENGRAM_ABI_VERSION 1
+#define TK_ENGRAM_MAX_H 8192
+
+/*
+ * Forward: zhichai.net TileKernels page, section "5. Engram", gate formula
+ * (engram_gate_fwd fuses RMSNorm, signed-sqrt and the sigmoid gate).
+ *
+ *   x, k, v : bf16 [T, H]  inputs (x is the formula's hidden_states)
+ *   wh, we  : fp32 [H]     RMSNorm weights of x and of k
+ *   out     : bf16 [T, H]  out = x + gate * v
+ *   gate    : fp32 [T]     the gate of each token
+ *   eps     : RMSNorm epsilon (inside the square root), finite and > 0
+ */
+tk_status tk_engram_gate_fwd(const uint16_t* x, const uint16_t* k,
+                             const uint16_t* v, const float* wh,
+                             const float* we, uint16_t* out, float* gate,
+                             int64_t T, int64_t H, double eps, void* stream);
+
+/*
+ * Number of weight-gradient partial rows P the backward writes for (T, H):
+ * the tokens are cut into P contiguous blocks, each reduced by one
+ * workgroup. A pure function of (T, H); 0 when T = 0.
+ */
+int64_t tk_engram_num_partials(int64_t T, int64_t H);
+
+/* Bytes of backward workspace needed for (T, H): P * H * sizeof(float). */
+size_t tk_engram_bwd_workspace_bytes(int64_t T, int64_t H);
+
+/*
+ * Backward of the forward above (section "5. Engram": engram_gate_bwd), by
+ * the chain rule through out = x + gate * v, the sigmoid, signed_sqrt, the
+ * scalar, the dot product and both RMSNorms.
+ *
+ *   grad_out        : bf16 [T, H]  dL/d out
+ *   x, k, v, wh, we : as for the forward
+ *   dx, dk, dv      : bf16 [T, H]  dL/dx, dL/dk, dL/dv
+ *   workspace       : fp32 [P, H]  per-block weight-gradient partials
+ *                     c_p[i] = sum over the block's tokens t of
+ *                              dd_t * r_x,t * r_k,t * x_t,i * k_t,i
+ *                     with dd_t = dL/dd_t; input to tk_engram_grad_w_reduce
+ *   workspace_bytes : size of `workspace`, at least
+ *                     tk_engram_bwd_workspace_bytes(T, H)
+ *   eps             : as for the forward
+ *   dsqrt_clamp     : the derivative of signed_sqrt, 1 / (2 sqrt|z|), is
+ *                     evaluated as 1 / (2 sqrt(max(|z|, dsqrt_clamp))) so it
+ *                     stays finite at z = 0 (the page gives no value there);
+ *                     finite and > 0
+ *
+ * The gate is recomputed from x and k exactly as the forward computes it.
+ */
+tk_status tk_engram_gate_bwd(const uint16_t* grad_out, const uint16_t* x,
+                             const uint16_t* k, const uint16_t* v,
+                             const float* wh, const float* we, uint16_t* dx,
+                             uint16_t* dk, uint16_t* dv, float* workspace,
+                             size_t workspace_bytes, int64_t T, int64_t H,
+                             double eps, double dsqrt_clamp, void* stream);
+
+/*
+ * Weight-gradient reduction (section "5. Engram": engram_grad_w_reduce): a
+ * fixed-order tree over the P partial rows written by tk_engram_gate_bwd,
+ *   c[i]   = sum_p workspace[p, i]
+ *   dwh[i] = we[i] * c[i]      (dL/dwh)
+ *   dwe[i] = wh[i] * c[i]      (dL/dwe)
+ * since dL/dwh_i = sum_t dd_t r_x,t x_t,i * (r_k,t k_t,i we_i) and likewise
+ * for we. P = 0 writes zeros.
+ *
+ *   workspace : fp32 [P, H], P = tk_engram_num_partials(T, H)
+ *   wh, we    : fp32 [H]
+ *   dwh, dwe  : fp32 [H]
+ */
+tk_status tk_engram_grad_w_reduce(const float* workspace, int64_t P, int64_t H,
+                                  const float* wh, const float* we, float* dwh,
+                                  float* dwe, void* stream);
+
+/*
+ * Measurement aid, not part of the gate: copies `bytes` bytes (a multiple
+ * of 16, both pointers 16-byte aligned) with the same 128-bit access width
+ * as the gate kernels, to calibrate hardware byte counters and to give the
+ * practical HBM ceiling of the device it runs on.
+ */
+tk_status tk_engram_copy_probe(const void* src, void* dst, size_t bytes,
+                               void* stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char* tk_status_string(tk_status s);
+
+/* TK_ENGRAM_ABI_VERSION of the built library. */
+int32_t tk_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TK_ENGRAM_H */

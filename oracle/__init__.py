@@ -19,6 +19,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "engram_oracle.cpp")
+_SRC_CMP = os.path.join(_HERE, "compare.cpp")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
 EPS = 1e-6          # RMSNorm epsilon used throughout (the pages give none)
@@ -28,7 +29,7 @@ CLAMP = 1e-4        # lower clamp of |z| in the signed-sqrt derivative
 def build(verbose: bool = False) -> str:
     """Compile the oracle with g++ (no fast-math, no FMA contraction)."""
     cmd = ["g++", "-O2", "-std=c++17", "-ffp-contract=off", "-fPIC", "-shared",
-           "-pthread", _SRC, "-o", _LIB]
+           "-pthread", _SRC, _SRC_CMP, "-o", _LIB]
     if verbose:
         print(" ".join(cmd))
     subprocess.run(cmd, check=True)
@@ -52,8 +53,11 @@ def lib() -> ctypes.CDLL:
         L.oracle_bwd_bf16.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, dbl, dbl,
                                       vp, vp, vp, vp, vp, vp, i32]
         L.oracle_round_bf16.argtypes = [vp, i64, vp]
+        L.oracle_compare_bf16.argtypes = [vp, vp, i64, i64, vp, vp, i32]
+        L.oracle_check_out.argtypes = [vp, vp, vp, vp, vp, i64, i64, vp, i32]
         for n in ("oracle_fwd_f64", "oracle_bwd_f64", "oracle_fwd_bf16",
-                  "oracle_bwd_bf16", "oracle_round_bf16"):
+                  "oracle_bwd_bf16", "oracle_round_bf16", "oracle_compare_bf16",
+                  "oracle_check_out"):
             getattr(L, n).restype = None
         L.oracle_fwd_stats_width.restype = i32
         L.oracle_bwd_stats_width.restype = i32
@@ -147,3 +151,58 @@ def round_bf16(a) -> np.ndarray:
 def bf16_to_f64(bits) -> np.ndarray:
     bits = np.asarray(bits, dtype=np.uint16)
     return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+# ---- comparison statistics (test infrastructure) -------------------------------
+
+class BF16Stats:
+    """Streaming error statistics of bf16 GPU results against the oracle's fp64
+    values rounded to bf16, split by row class (0 = regular rows)."""
+
+    CLASSES = 4
+
+    def __init__(self):
+        self.acc = np.zeros(self.CLASSES * 6)
+
+    def add(self, gpu_bits, ref, row_class=None, threads=None):
+        rows, H = ref.shape
+        assert gpu_bits.shape == (rows, H) and gpu_bits.dtype == np.uint16
+        gpu_bits = np.ascontiguousarray(gpu_bits)
+        ref = np.ascontiguousarray(ref, dtype=np.float64)
+        rc = None if row_class is None else np.ascontiguousarray(row_class, dtype=np.uint8)
+        lib().oracle_compare_bf16(_p(gpu_bits), _p(ref), rows, H, _p(rc), _p(self.acc),
+                                  threads or default_threads())
+
+    def _cls(self, classes):
+        a = self.acc.reshape(self.CLASSES, 6)
+        return a[list(classes)]
+
+    def rel_l2(self, classes=(0, 1, 2, 3)):
+        a = self._cls(classes)
+        den = a[:, 1].sum()
+        return float(np.sqrt(a[:, 0].sum() / den)) if den > 0 else float(a[:, 0].sum() > 0)
+
+    def max_ulp(self, classes=(0, 1, 2, 3)):
+        return float(self._cls(classes)[:, 2].max())
+
+    def count_over_1ulp(self, classes=(0, 1, 2, 3)):
+        return int(self._cls(classes)[:, 3].sum())
+
+    def max_row_rel(self, classes=(0, 1, 2, 3)):
+        return float(self._cls(classes)[:, 4].max())
+
+    def nonfinite(self):
+        return int(self.acc.reshape(self.CLASSES, 6)[:, 5].sum())
+
+
+def check_out(gpu_bits, ref, x_bits, v_bits, gate, res=None, threads=None):
+    """Accumulate the forward-output check; returns res = [max ulp, n > 1 ulp,
+    n passing by the cancellation bound, n failing]."""
+    rows, H = ref.shape
+    res = np.zeros(4) if res is None else res
+    arrs = [np.ascontiguousarray(a) for a in (gpu_bits, x_bits, v_bits)]
+    ref = np.ascontiguousarray(ref, dtype=np.float64)
+    gate = np.ascontiguousarray(gate, dtype=np.float64)
+    lib().oracle_check_out(_p(arrs[0]), _p(ref), _p(arrs[1]), _p(arrs[2]), _p(gate),
+                           rows, H, _p(res), threads or default_threads())
+    return res

@@ -161,6 +161,50 @@ void run_threads(int64_t rows, int nthreads, F fn) {
   for (auto& th : pool) th.join();
 }
 
+// Round fp64 values to bf16 bit patterns, to nearest with ties to even.
+// The comparison convention for bf16 outputs is "the oracle's fp64 value,
+// rounded once to bf16".
+//
+// Normal bf16 range: bf16 keeps the sign, the exponent and the top 7 stored
+// significand bits of the value, so the fp64 significand (52 stored bits) is
+// cut after its 7th bit and rounded on the 45 bits dropped. Elsewhere
+// (subnormal bf16, overflow, zero, NaN) the value is rounded by scaling.
+uint16_t round_one(double val) {
+  uint64_t b;
+  std::memcpy(&b, &val, 8);
+  const uint64_t sign = b >> 63;
+  const int exp_field = (int)((b >> 52) & 0x7FF);
+  const int e = exp_field - 1023;                     // val = 1.f * 2^e
+  if (exp_field != 0 && exp_field != 0x7FF && e >= -126 && e <= 127) {
+    const uint64_t frac = b & ((1ull << 52) - 1);
+    uint64_t keep = frac >> 45;                       // 7 stored bits
+    const uint64_t dropped = frac & ((1ull << 45) - 1);
+    const uint64_t half = 1ull << 44;
+    uint64_t biased = (uint64_t)(e + 127);
+    if (dropped > half || (dropped == half && (keep & 1))) {
+      ++keep;
+      if (keep == 128) {                              // significand overflow
+        keep = 0;
+        ++biased;
+      }
+    }
+    if (biased >= 255) return (uint16_t)((sign << 15) | 0x7F80);
+    return (uint16_t)((sign << 15) | (biased << 7) | keep);
+  }
+  if (std::isnan(val)) return 0x7FC0;
+  const uint16_t sbit = (uint16_t)(sign << 15);
+  double mag = std::fabs(val);
+  if (mag == 0.0) return sbit;
+  if (e > 127) return sbit | 0x7F80;                  // beyond the bf16 range
+  // |val| < 2^-126: bf16 subnormals are multiples of 2^-133.
+  const double units = mag * 0x1p133;                 // exact scaling
+  double lo = std::floor(units);
+  const double frac = units - lo;
+  if (frac > 0.5 || (frac == 0.5 && std::fmod(lo, 2.0) != 0.0)) lo += 1.0;
+  // lo <= 2^7: 2^7 itself is the smallest normal 2^-126 (bits 0x0080).
+  return sbit | (uint16_t)lo;
+}
+
 }  // namespace
 
 extern "C" {
@@ -289,44 +333,8 @@ void oracle_bwd_bf16(const uint16_t* gout, const uint16_t* x, const uint16_t* k,
   }
 }
 
-// Round fp64 values to bf16 bit patterns, to nearest with ties to even.
-// The comparison convention for bf16 outputs is "the oracle's fp64 value,
-// rounded once to bf16".
 void oracle_round_bf16(const double* v, int64_t n, uint16_t* out) {
-  for (int64_t j = 0; j < n; ++j) {
-    double val = v[j];
-    if (std::isnan(val)) {
-      out[j] = 0x7FC0;
-      continue;
-    }
-    uint16_t sign = std::signbit(val) ? 0x8000 : 0;
-    double mag = std::fabs(val);
-    if (mag == 0.0) {
-      out[j] = sign;
-      continue;
-    }
-    // bf16 has an 8-bit significand; its spacing in [2^e, 2^(e+1)) is 2^(e-7),
-    // and never finer than the subnormal spacing 2^-133.
-    int e = (int)std::floor(std::log2(mag));
-    if (std::ldexp(1.0, e) > mag) --e;          // guard log2 rounding
-    if (std::ldexp(1.0, e + 1) <= mag) ++e;
-    int spacing_exp = std::max(e - 7, -133);
-    double q = std::ldexp(1.0, spacing_exp);
-    double n_units = mag / q;                   // exact: a power-of-two scale
-    double lo = std::floor(n_units);
-    double frac = n_units - lo;
-    double units = lo;
-    if (frac > 0.5 || (frac == 0.5 && std::fmod(lo, 2.0) != 0.0)) units = lo + 1.0;
-    double r = units * q;
-    if (r >= 0x1p128) {
-      out[j] = sign | 0x7F80;
-      continue;
-    }
-    float f = (float)r;
-    uint32_t bits;
-    std::memcpy(&bits, &f, 4);
-    out[j] = sign | (uint16_t)((bits >> 16) & 0x7FFF);
-  }
+  for (int64_t j = 0; j < n; ++j) out[j] = round_one(v[j]);
 }
 
 }  // extern "C"

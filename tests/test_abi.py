@@ -1,0 +1,160 @@
+"""The C ABI without a GPU: the library loads, exports what the header
+declares, and rejects bad arguments before any device work."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import engram_conditional_memory_amd as eg
+from engram_conditional_memory_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tk_engram.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(eg.LIBRARY_PATH),
+                                reason="libtk_engram.so not built")
+
+A16 = 0x10000          # a 16-byte-aligned fake device address (never dereferenced)
+A4 = 0x10004
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tk_\w+)\s*\(", text)))
+
+
+def test_header_and_library_exports_agree():
+    names = declared_functions()
+    assert set(names) == set(B.EXPORTS)
+    lib = eg.load_library()
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings():
+    assert eg.tk_abi_version() == 1
+    seen = set()
+    for s in range(8):
+        msg = eg.tk_status_string(s)
+        assert msg and msg not in seen
+        seen.add(msg)
+    assert eg.tk_status_string(99) == "unknown status"
+
+
+def test_partials_are_a_function_of_shape():
+    assert eg.tk_engram_num_partials(0, 4096) == 0
+    assert eg.tk_engram_bwd_workspace_bytes(0, 4096) == 0
+    for T, H in ((1, 8), (64, 256), (1024, 4096), (16384, 4096), (32768, 7168),
+                 (65537, 7168)):
+        P = eg.tk_engram_num_partials(T, H)
+        assert 1 <= P <= min(T, 512)
+        rpb = -(-T // P)
+        assert (P - 1) * rpb < T            # every block owns at least one row
+        assert eg.tk_engram_bwd_workspace_bytes(T, H) == P * H * 4
+    assert eg.tk_engram_num_partials(64, 12) == 0      # invalid shapes give 0
+    assert eg.tk_engram_num_partials(-1, 64) == 0
+
+
+def fwd(**kw):
+    a = dict(x=A16, k=A16, v=A16, wh=A16, we=A16, out=A16, gate=A16, T=4, H=64,
+             eps=1e-6)
+    a.update(kw)
+    return eg.load_library().tk_engram_gate_fwd(
+        a["x"], a["k"], a["v"], a["wh"], a["we"], a["out"], a["gate"], a["T"], a["H"],
+        a["eps"], None)
+
+
+def bwd(**kw):
+    a = dict(g=A16, x=A16, k=A16, v=A16, wh=A16, we=A16, dx=A16, dk=A16, dv=A16,
+             ws=A16, wsb=1 << 30, T=4, H=64, eps=1e-6, clamp=1e-4)
+    a.update(kw)
+    return eg.load_library().tk_engram_gate_bwd(
+        a["g"], a["x"], a["k"], a["v"], a["wh"], a["we"], a["dx"], a["dk"], a["dv"],
+        a["ws"], a["wsb"], a["T"], a["H"], a["eps"], a["clamp"], None)
+
+
+def red(**kw):
+    a = dict(ws=A16, P=3, H=64, wh=A16, we=A16, dwh=A16, dwe=A16)
+    a.update(kw)
+    return eg.load_library().tk_engram_grad_w_reduce(
+        a["ws"], a["P"], a["H"], a["wh"], a["we"], a["dwh"], a["dwe"], None)
+
+
+def test_forward_argument_checks():
+    assert fwd(T=-1) == B.TK_ERR_SHAPE
+    assert fwd(H=0) == B.TK_ERR_SHAPE
+    assert fwd(H=12) == B.TK_ERR_ALIGN
+    assert fwd(H=8200) == B.TK_ERR_UNSUPPORTED
+    assert fwd(eps=0.0) == B.TK_ERR_VALUE
+    assert fwd(eps=float("nan")) == B.TK_ERR_VALUE
+    assert fwd(T=0, x=None) == B.TK_SUCCESS          # empty: nothing to do
+    for name in ("x", "k", "v", "wh", "we", "out", "gate"):
+        assert fwd(**{name: None}) == B.TK_ERR_NULL, name
+    for name in ("x", "k", "v", "wh", "we", "out"):
+        assert fwd(**{name: A16 + 8}) == B.TK_ERR_ALIGN, name
+    assert fwd(gate=A16 + 2) == B.TK_ERR_ALIGN
+
+
+def test_backward_argument_checks():
+    assert bwd(T=-3) == B.TK_ERR_SHAPE
+    assert bwd(H=20) == B.TK_ERR_ALIGN
+    assert bwd(H=16384) == B.TK_ERR_UNSUPPORTED
+    assert bwd(clamp=0.0) == B.TK_ERR_VALUE
+    assert bwd(clamp=float("inf")) == B.TK_ERR_VALUE
+    assert bwd(T=0, ws=None, wsb=0) == B.TK_SUCCESS
+    for name in ("g", "x", "k", "v", "wh", "we", "dx", "dk", "dv", "ws"):
+        assert bwd(**{name: None}) == B.TK_ERR_NULL, name
+        assert bwd(**{name: A4}) == B.TK_ERR_ALIGN, name
+    need = eg.tk_engram_bwd_workspace_bytes(4, 64)
+    assert bwd(wsb=need - 4) == B.TK_ERR_WORKSPACE
+
+
+def test_reduce_argument_checks():
+    assert red(P=-1) == B.TK_ERR_SHAPE
+    assert red(H=-8) == B.TK_ERR_SHAPE
+    assert red(H=36) == B.TK_ERR_ALIGN
+    assert red(H=9000) == B.TK_ERR_UNSUPPORTED
+    for name in ("ws", "wh", "we", "dwh", "dwe"):
+        assert red(**{name: None}) == B.TK_ERR_NULL, name
+        assert red(**{name: A4}) == B.TK_ERR_ALIGN, name
+
+
+def test_copy_probe_argument_checks():
+    L = eg.load_library()
+    assert L.tk_engram_copy_probe(None, None, 0, None) == B.TK_SUCCESS
+    assert L.tk_engram_copy_probe(None, A16, 64, None) == B.TK_ERR_NULL
+    assert L.tk_engram_copy_probe(A16, A16, 40, None) == B.TK_ERR_ALIGN
+    assert L.tk_engram_copy_probe(A4, A16, 64, None) == B.TK_ERR_ALIGN
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    x = torch.zeros(4, 64, dtype=torch.bfloat16)
+    w = torch.ones(64)
+    with pytest.raises(ValueError):
+        eg.tk_engram_gate_fwd(x, x, x, w, w)
+
+
+def test_missing_library_raises(tmp_path):
+    old = B._lib
+    try:
+        B._lib = None
+        with pytest.raises(RuntimeError, match="missing"):
+            B.load_library(str(tmp_path / "nope.so"))
+    finally:
+        B._lib = old
+
+
+def test_product_path_does_not_touch_the_oracle():
+    # The library and its binding neither import nor link the oracle.
+    pkg = os.path.join(ROOT, "engram_conditional_memory_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f), encoding="utf-8").read()
+                assert "oracle" not in text.lower(), f
+    with open(eg.LIBRARY_PATH, "rb") as fh:
+        assert b"oracle_" not in fh.read()

@@ -1,0 +1,277 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 oracle.
+
+Tolerances (written here, derived in the design notes):
+  gate            max |gpu - oracle| <= 1e-5
+  out             within 1 bf16 ulp of bf16(oracle), or, where x and gate*v
+                  cancel, |gpu - oracle| <= 1e-5 |v| + 2^-24 (|x| + |gate v|)
+  dx, dk, dv      relative L2 error <= 1e-3 against bf16(oracle)
+  dwh, dwe        relative L2 error <= 1e-3 against the oracle (fp32 outputs)
+  reruns          bit-identical
+Full-size workloads are compared on every element, streaming the oracle over
+chunks of rows.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+GATE_TOL = 1e-5
+REL_TOL = 1e-3
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def eg(cuda_device):
+    import engram_conditional_memory_amd as m
+    m.load_library()
+    return m
+
+
+def to_dev(bits, dev):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+
+def to_host_bits(t):
+    import torch
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def run_gpu(eg, d, dev, backward=True):
+    """Forward (+ backward + reduction) on the GPU; returns host arrays."""
+    import torch
+    T, H = d["x"].shape
+    x, k, v = to_dev(d["x"], dev), to_dev(d["k"], dev), to_dev(d["v"], dev)
+    wh = torch.from_numpy(d["wh"]).to(dev)
+    we = torch.from_numpy(d["we"]).to(dev)
+    out, gate = eg.tk_engram_gate_fwd(x, k, v, wh, we)
+    res = {}
+    if backward:
+        g = to_dev(d["grad_out"], dev)
+        dx, dk, dv, ws, P = eg.tk_engram_gate_bwd(g, x, k, v, wh, we)
+        dwh, dwe = eg.tk_engram_grad_w_reduce(ws, P, H, wh, we)
+        torch.cuda.synchronize()
+        del g
+        res.update(dx=to_host_bits(dx), dk=to_host_bits(dk), dv=to_host_bits(dv),
+                   dwh=dwh.cpu().numpy(), dwe=dwe.cpu().numpy(), P=P)
+        del dx, dk, dv, ws
+    torch.cuda.synchronize()
+    res.update(out=to_host_bits(out), gate=gate.cpu().numpy())
+    del x, k, v, out, gate
+    torch.cuda.empty_cache()
+    return res
+
+
+def row_classes(d):
+    """0 = regular row, 1 = some input row of the token is all zero,
+    2 = some input row is scaled by 1e3 (stress workload only)."""
+    T = d["x"].shape[0]
+    cls = np.zeros(T, dtype=np.uint8)
+    if d["config"].kind != "stress":
+        return cls
+    for name in ("x", "k", "v"):
+        s = synth.stress_row_scales(0, d["T"], name)[d["r0"]:d["r0"] + T]
+        cls[s == 1e3] = np.maximum(cls[s == 1e3], 2)
+        cls[s == 0.0] = 1
+    return cls
+
+
+def compare(d, g, backward=True, chunk=2048):
+    """Stream the oracle over the rows and collect every statistic."""
+    T, H = d["x"].shape
+    cls = row_classes(d)
+    out_res = np.zeros(4)
+    gate_err = 0.0
+    st = {n: oracle.BF16Stats() for n in ("dx", "dk", "dv")}
+    dwh = np.zeros(H)
+    dwe = np.zeros(H)
+    min_abs_z = np.inf
+    for a in range(0, T, chunk):
+        b = min(T, a + chunk)
+        sl = slice(a, b)
+        o_out, o_gate, o_z = oracle.fwd_bf16(d["x"][sl], d["k"][sl], d["v"][sl],
+                                             d["wh"], d["we"])
+        gate_err = max(gate_err, float(np.max(np.abs(g["gate"][sl] - o_gate))))
+        nz = np.abs(o_z[o_z != 0])
+        if nz.size:
+            min_abs_z = min(min_abs_z, float(nz.min()))
+        oracle.check_out(g["out"][sl], o_out, d["x"][sl], d["v"][sl], o_gate, out_res)
+        del o_out
+        if backward:
+            o_dx, o_dk, o_dv, p_wh, p_we, _ = oracle.bwd_bf16(
+                d["grad_out"][sl], d["x"][sl], d["k"][sl], d["v"][sl], d["wh"], d["we"])
+            st["dx"].add(g["dx"][sl], o_dx, cls[sl])
+            st["dk"].add(g["dk"][sl], o_dk, cls[sl])
+            st["dv"].add(g["dv"][sl], o_dv, cls[sl])
+            dwh += p_wh
+            dwe += p_we
+            del o_dx, o_dk, o_dv
+    rep = {"gate_err": gate_err, "out": out_res, "min_abs_z": min_abs_z}
+    if backward:
+        rep.update(st=st, dwh_rel=float(np.linalg.norm(g["dwh"] - dwh) / np.linalg.norm(dwh)),
+                   dwe_rel=float(np.linalg.norm(g["dwe"] - dwe) / np.linalg.norm(dwe)))
+    return rep
+
+
+def assert_report(rep, backward=True, name=""):
+    out = rep["out"]
+    say(f"[{name}] gate max err {rep['gate_err']:.3e} (min |z| {rep['min_abs_z']:.2e}); "
+        f"out max ulp {out[0]:.0f}, >1ulp {out[1]:.0f}, by cancellation bound "
+        f"{out[2]:.0f}, failing {out[3]:.0f}")
+    assert rep["gate_err"] <= GATE_TOL
+    assert out[3] == 0
+    if backward:
+        for n, s in rep["st"].items():
+            say(f"[{name}] {n}: rel L2 {s.rel_l2():.3e} (regular rows {s.rel_l2([0]):.3e}), "
+                f"max row rel {s.max_row_rel():.3e}, max ulp {s.max_ulp():.0f}, "
+                f"non-finite {s.nonfinite()}")
+            assert s.nonfinite() == 0
+            assert s.rel_l2() <= REL_TOL, n
+            assert s.rel_l2([0]) <= REL_TOL, n
+        say(f"[{name}] dwh rel L2 {rep['dwh_rel']:.3e}, dwe rel L2 {rep['dwe_rel']:.3e}")
+        assert rep["dwh_rel"] <= REL_TOL and rep["dwe_rel"] <= REL_TOL
+
+
+# ---------------------------------------------------------------- workloads
+
+def test_config1_tiny(eg, cuda_device):
+    d = synth.make_inputs(1)
+    g = run_gpu(eg, d, cuda_device)
+    rep = compare(d, g)
+    assert_report(rep, name="tiny T=64 H=256")
+    # the tiny workload is small enough for a strict elementwise check too
+    assert rep["st"]["dv"].max_ulp() <= 1
+
+
+def test_config2_forward(eg, cuda_device):
+    d = synth.make_inputs(2, with_grad=False)
+    g = run_gpu(eg, d, cuda_device, backward=False)
+    assert_report(compare(d, g, backward=False), backward=False, name="fwd T=1024 H=4096")
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("cfg", [3, 4, 5])
+def test_full_size(eg, cuda_device, cfg):
+    c = synth.CONFIGS[cfg]
+    say(f"[config {cfg}] {c.name}: generating T={c.T} H={c.H}")
+    d = synth.make_inputs(cfg)
+    g = run_gpu(eg, d, cuda_device)
+    say(f"[config {cfg}] GPU done (P={g['P']}), comparing with the oracle")
+    assert_report(compare(d, g), name=c.name)
+
+
+# ------------------------------------------------------------- determinism
+
+def test_reruns_are_bit_identical(eg, cuda_device):
+    d = synth.make_inputs(3, rows=(0, 4099))     # ragged: not a block multiple
+    a = run_gpu(eg, d, cuda_device)
+    b = run_gpu(eg, d, cuda_device)
+    for n in ("out", "gate", "dx", "dk", "dv", "dwh", "dwe"):
+        assert np.array_equal(a[n].view(np.uint8), b[n].view(np.uint8)), n
+
+
+# -------------------------------------------------------------- edge cases
+
+def make_case(T, H, seed=0, fill=None):
+    r = np.random.default_rng(seed)
+    d = {"T": T, "H": H, "r0": 0, "config": synth.CONFIGS[1]}
+    for n in ("x", "k", "v", "grad_out"):
+        d[n] = oracle.round_bf16(r.standard_normal((T, H)))
+    d["wh"] = (1 + 0.1 * r.standard_normal(H)).astype(np.float32)
+    d["we"] = (1 + 0.1 * r.standard_normal(H)).astype(np.float32)
+    if fill:
+        fill(d)
+    return d
+
+
+@pytest.mark.parametrize("T,H", [(1, 8), (3, 64), (5, 72), (7, 520), (9, 1032),
+                                 (33, 2048), (17, 4096), (11, 7168), (6, 8192),
+                                 (1000, 4096), (513, 7168), (4099, 256)])
+def test_shapes(eg, cuda_device, T, H):
+    d = make_case(T, H, seed=T * 7 + H)
+    g = run_gpu(eg, d, cuda_device)
+    assert_report(compare(d, g), name=f"T={T} H={H}")
+
+
+def test_special_rows(eg, cuda_device):
+    T, H = 12, 4096
+
+    def fill(d):
+        z = np.zeros(H, dtype=np.uint16)
+        d["x"][0] = z                            # zero hidden row
+        d["k"][1] = z                            # zero key row
+        d["x"][2] = d["k"][2] = d["v"][2] = z    # everything zero
+        d["v"][3] = z                            # no gradient reaches the gate
+        d["x"][4] = d["k"][4]                    # k = x
+        d["k"][5] = d["x"][5] ^ 0x8000           # k = -x: mirrored gate
+        d["x"][6, 1::2] = 0                      # orthogonal supports: gate 1/2
+        d["k"][6, 0::2] = 0
+        big = oracle.round_bf16(oracle.bf16_to_f64(d["x"][7]) * 1e3)
+        d["x"][7] = big                          # scaled row
+    d = make_case(T, H, seed=5, fill=fill)
+    g = run_gpu(eg, d, cuda_device)
+    assert_report(compare(d, g), name="special rows")
+    gate = g["gate"]
+    assert gate[0] == 0.5 and gate[1] == 0.5 and gate[2] == 0.5 and gate[6] == 0.5
+    # orthogonal supports: out = bf16(x + v / 2), bit for bit
+    want = oracle.round_bf16(oracle.bf16_to_f64(d["x"][6]) + 0.5 * oracle.bf16_to_f64(d["v"][6]))
+    assert np.array_equal(g["out"][6], want)
+    # zero row everywhere: dx = grad_out exactly, dk = 0, dv = grad_out / 2
+    assert np.array_equal(g["dx"][2], d["grad_out"][2])
+    assert np.all(oracle.bf16_to_f64(g["dk"][2]) == 0)
+    # v = 0: no gradient through the gate
+    assert np.array_equal(g["dx"][3], d["grad_out"][3])
+    assert np.all(oracle.bf16_to_f64(g["dk"][3]) == 0)
+    # mirrored gate
+    assert abs(gate[4] + gate[5] - 1.0) < 2e-6
+
+
+def test_empty_and_zero_partials(eg, cuda_device):
+    import torch
+    dev = cuda_device
+    H = 256
+    x = torch.empty((0, H), dtype=torch.bfloat16, device=dev)
+    wh = torch.ones(H, device=dev)
+    out, gate = eg.tk_engram_gate_fwd(x, x, x, wh, wh)
+    assert out.shape == (0, H) and gate.shape == (0,)
+    dx, dk, dv, ws, P = eg.tk_engram_gate_bwd(x, x, x, x, wh, wh)
+    assert P == 0
+    dwh = torch.full((H,), 7.0, device=dev)
+    dwe = torch.full((H,), 7.0, device=dev)
+    eg.tk_engram_grad_w_reduce(ws, 0, H, wh, wh, dwh, dwe)
+    torch.cuda.synchronize()
+    assert torch.all(dwh == 0) and torch.all(dwe == 0)
+
+
+def test_side_stream_and_identity(eg, cuda_device):
+    import torch
+    d = make_case(300, 4096, seed=11)
+    s = torch.cuda.Stream(cuda_device)
+    with torch.cuda.stream(s):
+        g = run_gpu(eg, d, cuda_device)
+    torch.cuda.synchronize()
+    rep = compare(d, g)
+    assert_report(rep, name="side stream")
+    # wh * dwh == we * dwe up to fp32 rounding of the two products
+    lhs = d["wh"].astype(np.float64) * g["dwh"]
+    rhs = d["we"].astype(np.float64) * g["dwe"]
+    assert np.max(np.abs(lhs - rhs)) <= 1e-6 * np.max(np.abs(lhs))
+
+
+def test_copy_probe(eg, cuda_device):
+    import torch
+    src = torch.arange(1 << 20, dtype=torch.int32, device=cuda_device)
+    dst = torch.zeros_like(src)
+    eg.tk_engram_copy_probe(src, dst)
+    torch.cuda.synchronize()
+    assert torch.equal(src, dst)
