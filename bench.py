@@ -7,10 +7,16 @@ all on the same stream, inputs already resident in HBM.
 Prints one JSON line: fwd+bwd tokens/s on the main workload, the roofline of
 the dominant kernel (HBM-bound; algorithmic bytes / average launch time from
 HIP events on the launch stream against 8 TB/s), the same figures for the
-other tuned width, a plain 128-bit copy as the practical HBM ceiling, and the
+other tuned width, a 128-bit tiled copy as the practical HBM ceiling, and the
 fp64 oracle's throughput on the host as a reported CPU baseline.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 4]
+
+With --traffic-from FETCH_CSV WRITE_CSV it runs no GPU work: it reads the
+counter_collection.csv files of two rocprofv3 --pmc runs of this script
+(FETCH_SIZE, then WRITE_SIZE), scales each counter by what it reads for the
+copy probe of known size in the same run, and writes the measured HBM bytes
+per launch of every kernel to profiles/traffic_<workload>.json.
 """
 
 from __future__ import annotations
@@ -74,27 +80,40 @@ class Workload:
         self.ws = torch.empty((max(1, self.P), H), dtype=torch.float32, device=dev)
         self.dwh = torch.empty((H,), dtype=torch.float32, device=dev)
         self.dwe = torch.empty((H,), dtype=torch.float32, device=dev)
-        self.eg = eg
+        # the three C-ABI calls of one step, arguments marshalled once
+        self.fwd = eg.bind_gate_fwd(self.x, self.k, self.v, self.wh, self.we, self.out,
+                                    self.gate)
+        self.bwd = eg.bind_gate_bwd(self.g, self.x, self.k, self.v, self.wh, self.we,
+                                    self.dx, self.dk, self.dv, self.ws)
+        self.red = eg.bind_grad_w_reduce(self.ws, self.P, self.H, self.wh, self.we,
+                                         self.dwh, self.dwe)
 
-    def step(self, ev=None):
-        eg = self.eg
-        if ev is not None:
-            ev[0].record()
-        eg.tk_engram_gate_fwd(self.x, self.k, self.v, self.wh, self.we, self.out, self.gate)
-        if ev is not None:
-            ev[1].record()
-        eg.tk_engram_gate_bwd(self.g, self.x, self.k, self.v, self.wh, self.we,
-                              self.dx, self.dk, self.dv, self.ws)
-        if ev is not None:
-            ev[2].record()
-        eg.tk_engram_grad_w_reduce(self.ws, self.P, self.H, self.wh, self.we,
-                                   self.dwh, self.dwe)
-        if ev is not None:
-            ev[3].record()
+    def step(self):
+        self.fwd()
+        self.bwd()
+        self.red()
 
     def free(self):
-        for n in ("x", "k", "v", "g", "out", "gate", "dx", "dk", "dv", "ws", "dwh", "dwe"):
+        for n in ("x", "k", "v", "g", "out", "gate", "dx", "dk", "dv", "ws", "dwh", "dwe",
+                  "fwd", "bwd", "red"):
             setattr(self, n, None)
+
+
+def avg_launch_us(fn, reps: int) -> float:
+    """Average duration of one call of `fn`, from HIP events on the launch
+    stream around `reps` back-to-back calls (the queue stays ahead of the
+    host, so the figure is the kernels' own time)."""
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return 1e3 * a.elapsed_time(b) / reps
 
 
 def time_workload(w: Workload, steps: int, warmup: int) -> dict:
@@ -102,41 +121,35 @@ def time_workload(w: Workload, steps: int, warmup: int) -> dict:
     for _ in range(warmup):
         w.step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record()
-    for i in range(steps):
-        w.step(evs[i])
+    for _ in range(steps):
+        w.step()
     stop.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    total_ms = start.elapsed_time(stop)
-    fwd = [e[0].elapsed_time(e[1]) for e in evs]
-    bwd = [e[1].elapsed_time(e[2]) for e in evs]
-    red = [e[2].elapsed_time(e[3]) for e in evs]
+    ms_step = start.elapsed_time(stop) / steps
+    # per-kernel averages: each call alone, back to back, same stream
+    f_us = avg_launch_us(w.fwd, steps)
+    b_us = avg_launch_us(w.bwd, steps)
+    r_us = avg_launch_us(w.red, steps)
     T, H = w.T, w.H
     ab = algorithmic_bytes(T, H)
-    ms_step = total_ms / steps
-    f_us, b_us, r_us = (1e3 * float(np.mean(a)) for a in (fwd, bwd, red))
-    res = {
+    return {
         "workload": w.c.name, "T": T, "H": H, "P": w.P,
         "ms_per_step": ms_step, "wall_s": wall,
         "tokens_per_s": T / (ms_step / 1e3),
-        "fwd": {"us": f_us, "us_median": 1e3 * float(np.median(fwd)),
-                "tokens_per_s": T / (f_us / 1e6), "bytes": ab["fwd"],
+        "fwd": {"us": f_us, "tokens_per_s": T / (f_us / 1e6), "bytes": ab["fwd"],
                 "GBps": ab["fwd"] / (f_us * 1e3), "frac": ab["fwd"] / (f_us * 1e3) / HBM_PEAK_GBPS},
-        "bwd_kernel": {"us": b_us, "us_median": 1e3 * float(np.median(bwd)), "bytes": ab["bwd"],
-                       "GBps": ab["bwd"] / (b_us * 1e3),
+        "bwd_kernel": {"us": b_us, "bytes": ab["bwd"], "GBps": ab["bwd"] / (b_us * 1e3),
                        "frac": ab["bwd"] / (b_us * 1e3) / HBM_PEAK_GBPS},
         "reduce_us": r_us,
         "bwd": {"us": b_us + r_us, "tokens_per_s": T / ((b_us + r_us) / 1e6),
                 "GBps": ab["bwd"] / ((b_us + r_us) * 1e3),
                 "frac": ab["bwd"] / ((b_us + r_us) * 1e3) / HBM_PEAK_GBPS},
     }
-    return res
 
 
 def copy_ceiling(nbytes: int, eg, dev, reps: int = 20) -> dict:
@@ -160,21 +173,31 @@ def copy_ceiling(nbytes: int, eg, dev, reps: int = 20) -> dict:
             "frac": 2 * nbytes / (us * 1e3) / HBM_PEAK_GBPS}
 
 
-def cpu_baseline(host: dict) -> dict:
+def cpu_baseline(host: dict, budget_s: float = 10.0) -> dict:
     """The fp64 oracle, as it stands, on the host cores: forward + backward
-    over every token of the workload once."""
+    (incl. dwh/dwe) over the workload's tokens in chunks, repeating passes
+    over the workload until `budget_s` of wall time is spent."""
     import oracle
     th = oracle.default_threads()
     T = host["x"].shape[0]
+    chunk = 4096
+    done = 0
     t0 = time.perf_counter()
-    oracle.fwd_bf16(host["x"], host["k"], host["v"], host["wh"], host["we"],
-                    want_out=True, threads=th)
-    oracle.bwd_bf16(host["grad_out"], host["x"], host["k"], host["v"], host["wh"],
-                    host["we"], threads=th)
+    while True:
+        a = done % T
+        sl = slice(a, min(T, a + chunk))
+        oracle.fwd_bf16(host["x"][sl], host["k"][sl], host["v"][sl], host["wh"],
+                        host["we"], want_out=True, threads=th)
+        oracle.bwd_bf16(host["grad_out"][sl], host["x"][sl], host["k"][sl],
+                        host["v"][sl], host["wh"], host["we"], threads=th)
+        done += sl.stop - sl.start
+        if time.perf_counter() - t0 >= budget_s:
+            break
     dt = time.perf_counter() - t0
-    return {"value": T / dt, "unit": "tokens/s", "cores": th, "kind": "oracle",
-            "sample": f"all {T} tokens of the workload, fp64 forward + backward "
-                      f"(incl. dwh/dwe), one pass, {dt:.2f} s wall"}
+    return {"value": done / dt, "unit": "tokens/s", "cores": th, "kind": "oracle",
+            "sample": f"{done} tokens ({done / T:.2f} passes over the {T}-token workload, "
+                      f"chunks of {chunk}), fp64 forward + backward incl. dwh/dwe, "
+                      f"{dt:.1f} s wall on {th} threads"}
 
 
 def measured_traffic(kernel: str, workload: str):
@@ -193,6 +216,52 @@ def measured_traffic(kernel: str, workload: str):
     return None if k is None else k.get("bytes_per_launch")
 
 
+def read_counter_csv(path: str, counter: str) -> dict:
+    """Mean value per dispatch of `counter`, by kernel base name."""
+    import csv
+    per = {}
+    for r in csv.DictReader(open(path)):
+        if r.get("Counter_Name") != counter:
+            continue
+        name = r["Kernel_Name"].replace("(anonymous namespace)::", "")
+        if name.startswith("void "):
+            name = name[len("void "):]
+        base = name.split("(")[0].split("<")[0].split("::")[-1].strip()
+        per.setdefault(base, []).append(float(r["Counter_Value"]))
+    return {k: float(np.mean(v)) for k, v in per.items()}
+
+
+def traffic_from_counters(fetch_csv: str, write_csv: str, workload: int) -> dict:
+    import synth
+    c = synth.CONFIGS[workload]
+    fetch = read_counter_csv(fetch_csv, "FETCH_SIZE")
+    write = read_counter_csv(write_csv, "WRITE_SIZE")
+    copy_bytes = 2 * c.T * c.H              # the copy probe reads and writes this
+    f_scale = copy_bytes / (1024.0 * fetch["copy_probe_kernel"])
+    w_scale = copy_bytes / (1024.0 * write["copy_probe_kernel"])
+    ab = algorithmic_bytes(c.T, c.H)
+    algo = {"gate_fwd_kernel": ab["fwd"], "gate_bwd_kernel": ab["bwd"]}
+    kernels = {}
+    for k in sorted(set(fetch) & set(write)):
+        rd = fetch[k] * 1024.0 * f_scale
+        wr = write[k] * 1024.0 * w_scale
+        kernels[k] = {"fetch_kib_per_dispatch": fetch[k], "write_kib_per_dispatch": write[k],
+                      "read_bytes": rd, "write_bytes": wr, "bytes_per_launch": rd + wr,
+                      "algorithmic_bytes": algo.get(k),
+                      "measured_over_algorithmic": (rd + wr) / algo[k] if k in algo else None}
+    rec = {"workload": c.name, "T": c.T, "H": c.H,
+           "kernel_source_sha256_16": kernel_source_hash(),
+           "calibration": {"copy_bytes_each_way": copy_bytes,
+                           "fetch_scale": f_scale, "write_scale": w_scale},
+           "kernels": kernels}
+    os.makedirs(PROFILES, exist_ok=True)
+    path = os.path.join(PROFILES, f"traffic_{c.name}.json")
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1, sort_keys=True)
+        f.write("\n")
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -203,7 +272,13 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true",
                     help="skip the second tuned width")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="summarise two rocprofv3 --pmc runs instead of benchmarking")
     args = ap.parse_args()
+    if args.traffic_from:
+        rec = traffic_from_counters(args.traffic_from[0], args.traffic_from[1], args.workload)
+        print(json.dumps(rec, indent=1, sort_keys=True))
+        return
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not "
               "supported (the path shards by tokens; see the design notes).", file=sys.stderr)

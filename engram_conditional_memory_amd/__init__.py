@@ -10,6 +10,10 @@ same names and only marshal torch tensors into it.
 
 from ._binding import (  # noqa: F401
     DSQRT_CLAMP,
+    BoundCall,
+    bind_gate_bwd,
+    bind_gate_fwd,
+    bind_grad_w_reduce,
     EPS,
     EXPORTS,
     TkError,

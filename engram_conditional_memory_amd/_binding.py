@@ -212,3 +212,72 @@ def tk_engram_copy_probe(src, dst, stream=None):
                                              _stream_handle(src.device, stream))
     _check("tk_engram_copy_probe", st)
     return dst
+
+
+# ---- pre-marshalled calls ---------------------------------------------------
+
+class BoundCall:
+    """One C-ABI call whose arguments were checked and marshalled once.
+
+    Calling it only enqueues the kernels (no tensor checks, no pointer
+    lookups), so a timing loop is never limited by Python overhead. It keeps
+    references to its tensors, which therefore stay allocated while it lives.
+    """
+
+    def __init__(self, name, fn, args, keep):
+        self._name, self._fn, self._args, self._keep = name, fn, tuple(args), keep
+
+    def __call__(self):
+        st = self._fn(*self._args)
+        if st != TK_SUCCESS:
+            _check(self._name, st)
+
+
+def bind_gate_fwd(x, k, v, wh, we, out, gate, eps=EPS, stream=None):
+    """tk_engram_gate_fwd with fixed arguments; see tk_engram_gate_fwd."""
+    torch = _torch()
+    T, H, dev = _rows(x)
+    bf, f32 = torch.bfloat16, torch.float32
+    args = [_need(x, "x", bf, (T, H), dev), _need(k, "k", bf, (T, H), dev),
+            _need(v, "v", bf, (T, H), dev), _need(wh, "wh", f32, (H,), dev),
+            _need(we, "we", f32, (H,), dev), _need(out, "out", bf, (T, H), dev),
+            _need(gate, "gate", f32, (T,), dev), ctypes.c_int64(T), ctypes.c_int64(H),
+            ctypes.c_double(eps), _stream_handle(dev, stream)]
+    return BoundCall("tk_engram_gate_fwd", load_library().tk_engram_gate_fwd, args,
+                     (x, k, v, wh, we, out, gate))
+
+
+def bind_gate_bwd(grad_out, x, k, v, wh, we, dx, dk, dv, workspace, eps=EPS,
+                  dsqrt_clamp=DSQRT_CLAMP, stream=None):
+    """tk_engram_gate_bwd with fixed arguments; see tk_engram_gate_bwd."""
+    torch = _torch()
+    T, H, dev = _rows(x)
+    bf, f32 = torch.bfloat16, torch.float32
+    if workspace.dtype != f32 or workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous fp32 GPU tensor")
+    args = [_need(grad_out, "grad_out", bf, (T, H), dev), _need(x, "x", bf, (T, H), dev),
+            _need(k, "k", bf, (T, H), dev), _need(v, "v", bf, (T, H), dev),
+            _need(wh, "wh", f32, (H,), dev), _need(we, "we", f32, (H,), dev),
+            _need(dx, "dx", bf, (T, H), dev), _need(dk, "dk", bf, (T, H), dev),
+            _need(dv, "dv", bf, (T, H), dev), ctypes.c_void_p(workspace.data_ptr()),
+            ctypes.c_size_t(workspace.numel() * 4), ctypes.c_int64(T), ctypes.c_int64(H),
+            ctypes.c_double(eps), ctypes.c_double(dsqrt_clamp), _stream_handle(dev, stream)]
+    return BoundCall("tk_engram_gate_bwd", load_library().tk_engram_gate_bwd, args,
+                     (grad_out, x, k, v, wh, we, dx, dk, dv, workspace))
+
+
+def bind_grad_w_reduce(workspace, P, H, wh, we, dwh, dwe, stream=None):
+    """tk_engram_grad_w_reduce with fixed arguments; see tk_engram_grad_w_reduce."""
+    torch = _torch()
+    dev = wh.device
+    f32 = torch.float32
+    if workspace.dtype != f32 or workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous fp32 tensor on wh's device")
+    if workspace.numel() < P * H:
+        raise ValueError("workspace holds fewer than P * H values")
+    args = [ctypes.c_void_p(workspace.data_ptr()), ctypes.c_int64(P), ctypes.c_int64(H),
+            _need(wh, "wh", f32, (H,), dev), _need(we, "we", f32, (H,), dev),
+            _need(dwh, "dwh", f32, (H,), dev), _need(dwe, "dwe", f32, (H,), dev),
+            _stream_handle(dev, stream)]
+    return BoundCall("tk_engram_grad_w_reduce", load_library().tk_engram_grad_w_reduce,
+                     args, (workspace, wh, we, dwh, dwe))

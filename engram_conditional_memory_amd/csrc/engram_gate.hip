@@ -88,7 +88,9 @@ __device__ __forceinline__ double wave_sum(double v) {
 
 // ---- per-thread slice of a row ---------------------------------------------
 
-// Chunk j of thread `tid` is 16-byte chunk j * NT + tid of the row.
+// Chunk j of thread `tid` is 16-byte chunk j * NT + tid of the row. Every row
+// is read and written exactly once, so loads and stores carry the
+// nontemporal hint (streamed, not kept in the caches).
 template <int NT, int C, bool FULL>
 __device__ __forceinline__ void load_row(const u32x4* __restrict__ row, int tid,
                                          int nchunk, u32x4 (&dst)[C]) {
@@ -96,20 +98,24 @@ __device__ __forceinline__ void load_row(const u32x4* __restrict__ row, int tid,
   for (int j = 0; j < C; ++j) {
     const int c = j * NT + tid;
     if (FULL || c < nchunk) {
-      dst[j] = row[c];
+      dst[j] = __builtin_nontemporal_load(row + c);
     } else {
       dst[j] = u32x4{0u, 0u, 0u, 0u};
     }
   }
 }
 
-// w_i = wh_i * we_i for the thread's columns, in fp32 (elementwise work of
-// the backward) and exactly in fp64 (the dot product).
+__device__ __forceinline__ void store_chunk(u32x4* __restrict__ p, const u32x4 v) {
+  __builtin_nontemporal_store(v, p);
+}
+
+// w_i = wh_i * we_i for the thread's columns, exactly (the product of two
+// fp32 values is exact in fp64). The elementwise backward uses its fp32
+// rounding, (float)w, which is the correctly rounded fp32 product.
 template <int NT, int C, bool FULL>
 __device__ __forceinline__ void load_weights(const f32x4* __restrict__ wh,
                                              const f32x4* __restrict__ we,
                                              int tid, int nchunk,
-                                             float (&w32)[C][8],
                                              double (&w64)[C][8]) {
 #pragma unroll
   for (int j = 0; j < C; ++j) {
@@ -123,12 +129,41 @@ __device__ __forceinline__ void load_weights(const f32x4* __restrict__ wh,
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      w32[j][e] = a0[e] * b0[e];
-      w32[j][e + 4] = a1[e] * b1[e];
       w64[j][e] = (double)a0[e] * (double)b0[e];
       w64[j][e + 4] = (double)a1[e] * (double)b1[e];
     }
   }
+}
+
+// Where a thread keeps w_i = wh_i * we_i (fp64) for its columns: in
+// registers, or in LDS as thread-private storage (each thread reads back
+// only what it wrote itself, so no barrier is needed), which frees 16 * C
+// VGPRs for deeper row prefetch. Element e of the thread's chunk j lives at
+// wl[e * NT * C + j * NT + tid], so a wave's reads are 64 consecutive
+// doubles.
+template <int C>
+struct WeightsReg {
+  double w[C][8];
+  __device__ __forceinline__ double get(int j, int e) const { return w[j][e]; }
+};
+
+template <int NT, int C>
+struct WeightsLds {
+  double* wl;
+  int tid;
+  __device__ __forceinline__ double get(int j, int e) const {
+    return wl[e * NT * C + j * NT + tid];
+  }
+};
+
+template <int NT, int C>
+__device__ __forceinline__ WeightsLds<NT, C> stage_weights(const double (&w64)[C][8],
+                                                           double* wl, int tid) {
+#pragma unroll
+  for (int j = 0; j < C; ++j)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) wl[e * NT * C + j * NT + tid] = w64[j][e];
+  return WeightsLds<NT, C>{wl, tid};
 }
 
 struct RowScalars {
@@ -152,133 +187,268 @@ __device__ __forceinline__ RowScalars row_gate(float sum_xx, float sum_kk,
   return s;
 }
 
+// Row pipelining. A workgroup keeps D row buffers in registers: while one
+// row is reduced and written, the loads of the next D - 1 rows it owns are in
+// flight. The buffers rotate by unrolling the row loop D times (no register
+// copies, which would make the compiler wait for the prefetch), and every
+// prefetch is issued unconditionally with its row index clamped to the
+// block's last row, so the final redundant loads re-read that row.
+//
+// Cross-wave sums go through LDS slots indexed by row parity: a slot is
+// rewritten two rows later, after every thread has passed the barrier of
+// the row in between, so one barrier per row suffices.
+
+// Which rows a workgroup walks: block b takes rows
+//   b * block_stride + i * row_step,  i = 0 .. rows_of(first) - 1,
+// never beyond T and at most `per_block` of them. Contiguous blocks are
+// (block_stride = rows per block, row_step = 1); interleaved blocks are
+// (block_stride = 1, row_step = number of blocks), which keeps the rows in
+// flight across the chip inside one sliding window of the tensors.
+struct RowWalk {
+  int64_t T;
+  int64_t block_stride;
+  int64_t row_step;
+  int64_t per_block;
+  __device__ __forceinline__ int64_t rows_of(int64_t first) const {
+    if (first >= T) return 0;
+    const int64_t n = (T - first + row_step - 1) / row_step;
+    return n < per_block ? n : per_block;
+  }
+};
+
 // ---- forward ---------------------------------------------------------------
 
-template <int W, int C, bool FULL>
+template <int C>
+struct FwdBuf {
+  u32x4 x[C], k[C], v[C];
+};
+
+template <int NT, int C, bool FULL>
+__device__ __forceinline__ void fwd_load(FwdBuf<C>& b, const u32x4* __restrict__ x,
+                                         const u32x4* __restrict__ k,
+                                         const u32x4* __restrict__ v, int64_t row,
+                                         int nchunk, int tid) {
+  const int64_t o = row * nchunk;
+  load_row<NT, C, FULL>(x + o, tid, nchunk, b.x);
+  load_row<NT, C, FULL>(k + o, tid, nchunk, b.k);
+  load_row<NT, C, FULL>(v + o, tid, nchunk, b.v);
+}
+
+template <int W, int C, bool FULL, class WT>
+__device__ __forceinline__ void fwd_row(const FwdBuf<C>& b, int64_t r, int slot,
+                                        int tid, int nchunk, const WT& w64,
+                                        float (&red_f)[2][2][W],
+                                        double (&red_d)[2][W],
+                                        u32x4* __restrict__ out,
+                                        float* __restrict__ gate, float eps,
+                                        float inv_h, float inv_sqrt_h) {
+  constexpr int NT = W * kWave;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  float sxx = 0.f, skk = 0.f;
+  double sxkw = 0.0;
+#pragma unroll
+  for (int j = 0; j < C; ++j) {
+    float xf[8], kf[8];
+    unpack8(b.x[j], xf);
+    unpack8(b.k[j], kf);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      sxx = fmaf(xf[e], xf[e], sxx);
+      skk = fmaf(kf[e], kf[e], skk);
+      // x_i k_i is exact in fp32 (two 8-bit significands)
+      sxkw = fma((double)(xf[e] * kf[e]), w64.get(j, e), sxkw);
+    }
+  }
+  sxx = wave_sum(sxx);
+  skk = wave_sum(skk);
+  sxkw = wave_sum(sxkw);
+  if (lane == 0) {
+    red_f[slot][0][wave] = sxx;
+    red_f[slot][1][wave] = skk;
+    red_d[slot][wave] = sxkw;
+  }
+  __syncthreads();
+  float txx = 0.f, tkk = 0.f;
+  double txkw = 0.0;
+#pragma unroll
+  for (int i = 0; i < W; ++i) {
+    txx += red_f[slot][0][i];
+    tkk += red_f[slot][1][i];
+    txkw += red_d[slot][i];
+  }
+  const RowScalars s = row_gate(txx, tkk, txkw, eps, inv_h, inv_sqrt_h);
+
+  const int64_t o = r * nchunk;
+#pragma unroll
+  for (int j = 0; j < C; ++j) {
+    const int c = j * NT + tid;
+    if (FULL || c < nchunk) {
+      float xf[8], vf[8], of[8];
+      unpack8(b.x[j], xf);
+      unpack8(b.v[j], vf);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) of[e] = fmaf(s.g, vf[e], xf[e]);
+      store_chunk(out + o + c, pack8(of));
+    }
+  }
+  if (tid == 0) gate[r] = s.g;
+}
+
+template <int W, int C, bool FULL, int D>
 __global__ __launch_bounds__(W * kWave) void gate_fwd_kernel(
     const u32x4* __restrict__ x, const u32x4* __restrict__ k,
     const u32x4* __restrict__ v, const f32x4* __restrict__ wh,
     const f32x4* __restrict__ we, u32x4* __restrict__ out,
-    float* __restrict__ gate, int64_t T, int nchunk, int64_t rows_per_block,
-    float eps, float inv_h, float inv_sqrt_h) {
+    float* __restrict__ gate, RowWalk walk, int nchunk, float eps, float inv_h,
+    float inv_sqrt_h) {
   constexpr int NT = W * kWave;
   const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
+  __shared__ float red_f[2][2][W];
+  __shared__ double red_d[2][W];
 
-  // Per-wave partial sums, double-buffered by row parity so that one barrier
-  // per row suffices.
-  __shared__ float red_xx[2][W];
-  __shared__ float red_kk[2][W];
-  __shared__ double red_xkw[2][W];
+  const int64_t first = (int64_t)blockIdx.x * walk.block_stride;
+  const int64_t n = walk.rows_of(first);
+  if (n <= 0) return;
+  const int64_t step = walk.row_step;
+  auto row = [&](int64_t i) { return first + (i < n ? i : n - 1) * step; };
 
-  float w32[C][8];
-  double w64[C][8];
-  load_weights<NT, C, FULL>(wh, we, tid, nchunk, w32, w64);
-
-  const int64_t r0 = (int64_t)blockIdx.x * rows_per_block;
-  const int64_t r1 = min(T, r0 + rows_per_block);
-  if (r0 >= r1) return;
-
-  u32x4 xa[C], ka[C], va[C];
-  load_row<NT, C, FULL>(x + r0 * nchunk, tid, nchunk, xa);
-  load_row<NT, C, FULL>(k + r0 * nchunk, tid, nchunk, ka);
-  load_row<NT, C, FULL>(v + r0 * nchunk, tid, nchunk, va);
-
-  for (int64_t r = r0; r < r1; ++r) {
-    const bool more = r + 1 < r1;
-    u32x4 xb[C], kb[C], vb[C];
-    if (more) {
-      const int64_t o = (r + 1) * nchunk;
-      load_row<NT, C, FULL>(x + o, tid, nchunk, xb);
-      load_row<NT, C, FULL>(k + o, tid, nchunk, kb);
-      load_row<NT, C, FULL>(v + o, tid, nchunk, vb);
-    }
-
-    float sxx = 0.f, skk = 0.f;
-    double sxkw = 0.0;
+  FwdBuf<C> buf[D];
 #pragma unroll
-    for (int j = 0; j < C; ++j) {
-      float xf[8], kf[8];
-      unpack8(xa[j], xf);
-      unpack8(ka[j], kf);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        sxx = fmaf(xf[e], xf[e], sxx);
-        skk = fmaf(kf[e], kf[e], skk);
-        sxkw = fma((double)(xf[e] * kf[e]), w64[j][e], sxkw);
-      }
-    }
-    sxx = wave_sum(sxx);
-    skk = wave_sum(skk);
-    sxkw = wave_sum(sxkw);
-    const int slot = (int)((r - r0) & 1);
-    if (lane == 0) {
-      red_xx[slot][wave] = sxx;
-      red_kk[slot][wave] = skk;
-      red_xkw[slot][wave] = sxkw;
-    }
-    __syncthreads();
-    float txx = 0.f, tkk = 0.f;
-    double txkw = 0.0;
-#pragma unroll
-    for (int i = 0; i < W; ++i) {
-      txx += red_xx[slot][i];
-      tkk += red_kk[slot][i];
-      txkw += red_xkw[slot][i];
-    }
-    const RowScalars s = row_gate(txx, tkk, txkw, eps, inv_h, inv_sqrt_h);
+  for (int s = 0; s + 1 < D; ++s) fwd_load<NT, C, FULL>(buf[s], x, k, v, row(s), nchunk, tid);
+  WeightsReg<C> w64;
+  load_weights<NT, C, FULL>(wh, we, tid, nchunk, w64.w);
 
-    const int64_t o = r * nchunk;
+  for (int64_t i = 0;; i += D) {
 #pragma unroll
-    for (int j = 0; j < C; ++j) {
-      const int c = j * NT + tid;
-      if (FULL || c < nchunk) {
-        float xf[8], vf[8], of[8];
-        unpack8(xa[j], xf);
-        unpack8(va[j], vf);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) of[e] = fmaf(s.g, vf[e], xf[e]);
-        out[o + c] = pack8(of);
-      }
-    }
-    if (tid == 0) gate[r] = s.g;
-
-    if (more) {
-#pragma unroll
-      for (int j = 0; j < C; ++j) {
-        xa[j] = xb[j];
-        ka[j] = kb[j];
-        va[j] = vb[j];
-      }
+    for (int s = 0; s < D; ++s) {
+      fwd_load<NT, C, FULL>(buf[(s + D - 1) % D], x, k, v, row(i + s + D - 1), nchunk,
+                            tid);
+      fwd_row<W, C, FULL>(buf[s], row(i + s), (int)((i + s) & 1), tid, nchunk, w64,
+                          red_f, red_d, out, gate, eps, inv_h, inv_sqrt_h);
+      if (i + s + 1 >= n) return;
     }
   }
 }
 
 // ---- backward --------------------------------------------------------------
 
-template <int W, int C, bool FULL>
+template <int C>
+struct BwdBuf {
+  u32x4 g[C], x[C], k[C], v[C];
+};
+
+template <int NT, int C, bool FULL>
+__device__ __forceinline__ void bwd_load(BwdBuf<C>& b, const u32x4* __restrict__ gout,
+                                         const u32x4* __restrict__ x,
+                                         const u32x4* __restrict__ k,
+                                         const u32x4* __restrict__ v, int64_t row,
+                                         int nchunk, int tid) {
+  const int64_t o = row * nchunk;
+  load_row<NT, C, FULL>(gout + o, tid, nchunk, b.g);
+  load_row<NT, C, FULL>(v + o, tid, nchunk, b.v);
+  load_row<NT, C, FULL>(x + o, tid, nchunk, b.x);
+  load_row<NT, C, FULL>(k + o, tid, nchunk, b.k);
+}
+
+template <int W, int C, bool FULL, class WT>
+__device__ __forceinline__ void bwd_row(const BwdBuf<C>& b, int64_t r, int slot,
+                                        int tid, int nchunk, const WT& w64,
+                                        float (&cacc)[C][8],
+                                        float (&red_f)[2][3][W],
+                                        double (&red_d)[2][W],
+                                        u32x4* __restrict__ dx,
+                                        u32x4* __restrict__ dk,
+                                        u32x4* __restrict__ dv, float eps,
+                                        float clamp, float inv_h,
+                                        float inv_sqrt_h) {
+  constexpr int NT = W * kWave;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  float sxx = 0.f, skk = 0.f, sgv = 0.f;
+  double sxkw = 0.0;
+#pragma unroll
+  for (int j = 0; j < C; ++j) {
+    float gf[8], xf[8], kf[8], vf[8];
+    unpack8(b.g[j], gf);
+    unpack8(b.v[j], vf);
+    unpack8(b.x[j], xf);
+    unpack8(b.k[j], kf);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      sgv = fmaf(gf[e], vf[e], sgv);
+      sxx = fmaf(xf[e], xf[e], sxx);
+      skk = fmaf(kf[e], kf[e], skk);
+      sxkw = fma((double)(xf[e] * kf[e]), w64.get(j, e), sxkw);
+    }
+  }
+  sxx = wave_sum(sxx);
+  skk = wave_sum(skk);
+  sgv = wave_sum(sgv);
+  sxkw = wave_sum(sxkw);
+  if (lane == 0) {
+    red_f[slot][0][wave] = sxx;
+    red_f[slot][1][wave] = skk;
+    red_f[slot][2][wave] = sgv;
+    red_d[slot][wave] = sxkw;
+  }
+  __syncthreads();
+  float txx = 0.f, tkk = 0.f, tgv = 0.f;
+  double txkw = 0.0;
+#pragma unroll
+  for (int i = 0; i < W; ++i) {
+    txx += red_f[slot][0][i];
+    tkk += red_f[slot][1][i];
+    tgv += red_f[slot][2][i];
+    txkw += red_d[slot][i];
+  }
+  const RowScalars s = row_gate(txx, tkk, txkw, eps, inv_h, inv_sqrt_h);
+  // gate = sigmoid(sq): d gate / d sq = g (1 - g);
+  // sq = signed_sqrt(z): d sq / dz = 1 / (2 sqrt(max(|z|, clamp)));
+  // z = d / sqrt(H).
+  const float ds = tgv * s.g * (1.0f - s.g);
+  const float dz = ds * 0.5f * __builtin_amdgcn_rsqf(fmaxf(fabsf(s.z), clamp));
+  const float dd = dz * inv_sqrt_h;
+  const float A = dd * s.r_x * s.r_k;
+  const float Bx = dd * s.r_x * s.r_x * s.d * inv_h;
+  const float Bk = dd * s.r_k * s.r_k * s.d * inv_h;
+
+  const int64_t o = r * nchunk;
+#pragma unroll
+  for (int j = 0; j < C; ++j) {
+    const int c = j * NT + tid;
+    if (FULL || c < nchunk) {
+      float gf[8], xf[8], kf[8], ox[8], ok[8], ov[8];
+      unpack8(b.g[j], gf);
+      unpack8(b.x[j], xf);
+      unpack8(b.k[j], kf);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float w = (float)w64.get(j, e);
+        ox[e] = fmaf(-Bx, xf[e], fmaf(A, w * kf[e], gf[e]));
+        ok[e] = fmaf(-Bk, kf[e], A * (w * xf[e]));
+        ov[e] = s.g * gf[e];
+        cacc[j][e] = fmaf(A, xf[e] * kf[e], cacc[j][e]);
+      }
+      store_chunk(dx + o + c, pack8(ox));
+      store_chunk(dk + o + c, pack8(ok));
+      store_chunk(dv + o + c, pack8(ov));
+    }
+  }
+}
+
+template <int W, int C, bool FULL, int D, bool WLDS>
 __global__ __launch_bounds__(W * kWave) void gate_bwd_kernel(
     const u32x4* __restrict__ gout, const u32x4* __restrict__ x,
     const u32x4* __restrict__ k, const u32x4* __restrict__ v,
     const f32x4* __restrict__ wh, const f32x4* __restrict__ we,
     u32x4* __restrict__ dx, u32x4* __restrict__ dk, u32x4* __restrict__ dv,
-    f32x4* __restrict__ partial, int64_t T, int nchunk,
-    int64_t rows_per_block, float eps, float clamp, float inv_h,
-    float inv_sqrt_h) {
+    f32x4* __restrict__ partial, RowWalk walk, int nchunk, float eps,
+    float clamp, float inv_h, float inv_sqrt_h) {
   constexpr int NT = W * kWave;
   const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
-
-  __shared__ float red_xx[2][W];
-  __shared__ float red_kk[2][W];
-  __shared__ float red_gv[2][W];
-  __shared__ double red_xkw[2][W];
-
-  float w32[C][8];
-  double w64[C][8];
-  load_weights<NT, C, FULL>(wh, we, tid, nchunk, w32, w64);
+  __shared__ float red_f[2][3][W];
+  __shared__ double red_d[2][W];
 
   // c_i over this block's rows, for the thread's columns.
   float cacc[C][8];
@@ -287,107 +457,41 @@ __global__ __launch_bounds__(W * kWave) void gate_bwd_kernel(
 #pragma unroll
     for (int e = 0; e < 8; ++e) cacc[j][e] = 0.f;
 
-  const int64_t r0 = (int64_t)blockIdx.x * rows_per_block;
-  const int64_t r1 = min(T, r0 + rows_per_block);
+  const int64_t first = (int64_t)blockIdx.x * walk.block_stride;
+  const int64_t n = walk.rows_of(first);
 
-  if (r0 < r1) {
-    u32x4 ga[C], xa[C], ka[C], va[C];
-    load_row<NT, C, FULL>(gout + r0 * nchunk, tid, nchunk, ga);
-    load_row<NT, C, FULL>(v + r0 * nchunk, tid, nchunk, va);
-    load_row<NT, C, FULL>(x + r0 * nchunk, tid, nchunk, xa);
-    load_row<NT, C, FULL>(k + r0 * nchunk, tid, nchunk, ka);
-
-    for (int64_t r = r0; r < r1; ++r) {
-      const bool more = r + 1 < r1;
-      u32x4 gb[C], xb[C], kb[C], vb[C];
-      if (more) {
-        const int64_t o = (r + 1) * nchunk;
-        load_row<NT, C, FULL>(gout + o, tid, nchunk, gb);
-        load_row<NT, C, FULL>(v + o, tid, nchunk, vb);
-        load_row<NT, C, FULL>(x + o, tid, nchunk, xb);
-        load_row<NT, C, FULL>(k + o, tid, nchunk, kb);
-      }
-
-      float sxx = 0.f, skk = 0.f, sgv = 0.f;
-      double sxkw = 0.0;
+  if (n > 0) {
+    const int64_t step = walk.row_step;
+    auto row = [&](int64_t i) { return first + (i < n ? i : n - 1) * step; };
+    BwdBuf<C> buf[D];
 #pragma unroll
-      for (int j = 0; j < C; ++j) {
-        float gf[8], xf[8], kf[8], vf[8];
-        unpack8(ga[j], gf);
-        unpack8(va[j], vf);
-        unpack8(xa[j], xf);
-        unpack8(ka[j], kf);
+    for (int s = 0; s + 1 < D; ++s)
+      bwd_load<NT, C, FULL>(buf[s], gout, x, k, v, row(s), nchunk, tid);
+    double w64[C][8];
+    load_weights<NT, C, FULL>(wh, we, tid, nchunk, w64);
+    auto walk_rows = [&](const auto& wts) {
+      for (int64_t i = 0;; i += D) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          sgv = fmaf(gf[e], vf[e], sgv);
-          sxx = fmaf(xf[e], xf[e], sxx);
-          skk = fmaf(kf[e], kf[e], skk);
-          sxkw = fma((double)(xf[e] * kf[e]), w64[j][e], sxkw);
+        for (int s = 0; s < D; ++s) {
+          bwd_load<NT, C, FULL>(buf[(s + D - 1) % D], gout, x, k, v,
+                                row(i + s + D - 1), nchunk, tid);
+          bwd_row<W, C, FULL>(buf[s], row(i + s), (int)((i + s) & 1), tid, nchunk,
+                              wts, cacc, red_f, red_d, dx, dk, dv, eps, clamp, inv_h,
+                              inv_sqrt_h);
+          if (i + s + 1 >= n) return;
         }
       }
-      sxx = wave_sum(sxx);
-      skk = wave_sum(skk);
-      sgv = wave_sum(sgv);
-      sxkw = wave_sum(sxkw);
-      const int slot = (int)((r - r0) & 1);
-      if (lane == 0) {
-        red_xx[slot][wave] = sxx;
-        red_kk[slot][wave] = skk;
-        red_gv[slot][wave] = sgv;
-        red_xkw[slot][wave] = sxkw;
-      }
-      __syncthreads();
-      float txx = 0.f, tkk = 0.f, tgv = 0.f;
-      double txkw = 0.0;
+    };
+    if constexpr (WLDS) {
+      __shared__ double wl[8 * NT * C];
+      walk_rows(stage_weights<NT, C>(w64, wl, tid));
+    } else {
+      WeightsReg<C> wr;
 #pragma unroll
-      for (int i = 0; i < W; ++i) {
-        txx += red_xx[slot][i];
-        tkk += red_kk[slot][i];
-        tgv += red_gv[slot][i];
-        txkw += red_xkw[slot][i];
-      }
-      const RowScalars s = row_gate(txx, tkk, txkw, eps, inv_h, inv_sqrt_h);
-      // gate = sigmoid(sq): d gate / d sq = g (1 - g);
-      // sq = signed_sqrt(z): d sq / dz = 1 / (2 sqrt(max(|z|, clamp)));
-      // z = d / sqrt(H).
-      const float ds = tgv * s.g * (1.0f - s.g);
-      const float dz = ds * 0.5f * __builtin_amdgcn_rsqf(fmaxf(fabsf(s.z), clamp));
-      const float dd = dz * inv_sqrt_h;
-      const float A = dd * s.r_x * s.r_k;
-      const float Bx = dd * s.r_x * s.r_x * s.d * inv_h;
-      const float Bk = dd * s.r_k * s.r_k * s.d * inv_h;
-
-      const int64_t o = r * nchunk;
+      for (int j = 0; j < C; ++j)
 #pragma unroll
-      for (int j = 0; j < C; ++j) {
-        const int c = j * NT + tid;
-        if (FULL || c < nchunk) {
-          float gf[8], xf[8], kf[8], ox[8], ok[8], ov[8];
-          unpack8(ga[j], gf);
-          unpack8(xa[j], xf);
-          unpack8(ka[j], kf);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            ox[e] = fmaf(-Bx, xf[e], fmaf(A, w32[j][e] * kf[e], gf[e]));
-            ok[e] = fmaf(-Bk, kf[e], A * (w32[j][e] * xf[e]));
-            ov[e] = s.g * gf[e];
-            cacc[j][e] = fmaf(A, xf[e] * kf[e], cacc[j][e]);
-          }
-          dx[o + c] = pack8(ox);
-          dk[o + c] = pack8(ok);
-          dv[o + c] = pack8(ov);
-        }
-      }
-
-      if (more) {
-#pragma unroll
-        for (int j = 0; j < C; ++j) {
-          ga[j] = gb[j];
-          xa[j] = xb[j];
-          ka[j] = kb[j];
-          va[j] = vb[j];
-        }
-      }
+        for (int e = 0; e < 8; ++e) wr.w[j][e] = w64[j][e];
+      walk_rows(wr);
     }
   }
 
@@ -405,11 +509,14 @@ __global__ __launch_bounds__(W * kWave) void gate_bwd_kernel(
 
 // ---- weight-gradient reduction -------------------------------------------
 
-// 256 threads: 16 groups of 4 columns x 16 strided slices of the partials.
-// Each thread sums its slice in increasing p; the 16 slice sums are then
-// added in increasing slice order. The order depends only on (P, H).
-constexpr int kRedCols4 = 16;
-constexpr int kRedSlices = 16;
+// 256 threads: kRedCols4 groups of 4 columns x kRedSlices strided slices of
+// the partials. Each thread sums its slice (partials p = slice, slice + S,
+// ...) in increasing p, with the loads of kRedUnroll partials in flight at a
+// time; the slice sums are then added in increasing slice order. The order
+// depends only on (P, H).
+constexpr int kRedCols4 = 8;
+constexpr int kRedSlices = 32;
+constexpr int kRedUnroll = 8;
 
 __global__ __launch_bounds__(kRedCols4* kRedSlices) void grad_w_reduce_kernel(
     const f32x4* __restrict__ partial, int64_t P, int nq,
@@ -421,7 +528,15 @@ __global__ __launch_bounds__(kRedCols4* kRedSlices) void grad_w_reduce_kernel(
   const int q = blockIdx.x * kRedCols4 + cx;
   f32x4 s = {0.f, 0.f, 0.f, 0.f};
   if (q < nq) {
-    for (int64_t p = py; p < P; p += kRedSlices) s += partial[p * nq + q];
+    int64_t p = py;
+    for (; p + (kRedUnroll - 1) * kRedSlices < P; p += kRedUnroll * kRedSlices) {
+      f32x4 t[kRedUnroll];
+#pragma unroll
+      for (int u = 0; u < kRedUnroll; ++u) t[u] = partial[(p + u * kRedSlices) * nq + q];
+#pragma unroll
+      for (int u = 0; u < kRedUnroll; ++u) s += t[u];
+    }
+    for (; p < P; p += kRedSlices) s += partial[p * nq + q];
   }
   part[py][cx] = s;
   __syncthreads();
@@ -436,37 +551,30 @@ __global__ __launch_bounds__(kRedCols4* kRedSlices) void grad_w_reduce_kernel(
 
 // ---- copy probe ------------------------------------------------------------
 
+// Each block copies contiguous 16 KiB tiles (256 threads x 4 chunks), tiles
+// dealt round-robin over the blocks; the remainder below one tile is copied
+// chunk by chunk. Nontemporal like the gate kernels.
+constexpr int kCopyUnroll = 4;
+
 __global__ __launch_bounds__(256) void copy_probe_kernel(
     const u32x4* __restrict__ src, u32x4* __restrict__ dst, int64_t n) {
-  const int64_t stride = (int64_t)gridDim.x * 256;
-  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  for (; i + 3 * stride < n; i += 4 * stride) {
-    u32x4 a = src[i], b = src[i + stride], c = src[i + 2 * stride],
-          d = src[i + 3 * stride];
-    dst[i] = a;
-    dst[i + stride] = b;
-    dst[i + 2 * stride] = c;
-    dst[i + 3 * stride] = d;
+  constexpr int64_t tile = 256 * kCopyUnroll;
+  const int64_t ntile = n / tile;
+  for (int64_t t = blockIdx.x; t < ntile; t += gridDim.x) {
+    const int64_t base = t * tile + threadIdx.x;
+    u32x4 a[kCopyUnroll];
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u)
+      a[u] = __builtin_nontemporal_load(src + base + u * 256);
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) store_chunk(dst + base + u * 256, a[u]);
   }
-  for (; i < n; i += stride) dst[i] = src[i];
+  for (int64_t i = ntile * tile + (int64_t)blockIdx.x * 256 + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * 256)
+    dst[i] = src[i];
 }
 
 // ---- host side -------------------------------------------------------------
-
-// Target number of row blocks; each block reduces its rows' weight-gradient
-// contribution into one partial row.
-constexpr int64_t kTargetBlocks = 512;
-
-int64_t rows_per_block(int64_t T) {
-  if (T <= 0) return 1;
-  return (T + kTargetBlocks - 1) / kTargetBlocks;
-}
-
-int64_t num_blocks(int64_t T) {
-  if (T <= 0) return 0;
-  const int64_t rpb = rows_per_block(T);
-  return (T + rpb - 1) / rpb;
-}
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -479,21 +587,46 @@ tk_status check_shape(int64_t T, int64_t H) {
 
 bool finite_positive(double a) { return std::isfinite(a) && a > 0.0; }
 
-// Launch shape for a row of nchunk 16-byte chunks: W waves, C chunks per
-// thread; FULL when W * 64 * C == nchunk exactly (no masking).
-struct Shape {
-  int W, C;
-  bool full;
+// Launch plan for a row of nchunk 16-byte chunks: W waves per row, C chunks
+// per thread (FULL when W * 64 * C == nchunk, i.e. no masking), D rows in
+// flight per workgroup, weights in LDS (backward), and G workgroups walking
+// the rows interleaved (block b takes rows b, b + G, ...). The two tuned
+// widths have plans measured on MI355X; other widths take the fewest waves
+// that cover the row. G is also the backward's number of weight-gradient
+// partials, so it depends only on (T, H).
+struct Plan {
+  int W, C, D;
+  bool full, wlds;
+  int64_t blocks;
 };
 
-Shape pick_shape(int nchunk) {
-  if (nchunk == 896) return {7, 2, true};   // H = 7168
-  if (nchunk == 512) return {4, 2, true};   // H = 4096
-  // Other widths: the fewest waves (1..8) that cover the row with one chunk
-  // per thread, else 8 waves with two; trailing chunks may be masked.
+Plan generic_plan(int nchunk) {
   for (int W = 1; W <= 8; W *= 2)
-    if (nchunk <= W * kWave) return {W, 1, nchunk == W * kWave};
-  return {8, 2, nchunk == 8 * kWave * 2};
+    if (nchunk <= W * kWave) return {W, 1, 2, nchunk == W * kWave, false, 256};
+  return {8, 2, 2, nchunk == 8 * kWave * 2, false, 256};
+}
+
+Plan fwd_plan(int nchunk) {
+  if (nchunk == 896) return {7, 2, 3, true, false, 192};   // H = 7168
+  if (nchunk == 512) return {8, 1, 2, true, false, 256};   // H = 4096
+  return generic_plan(nchunk);
+}
+
+Plan bwd_plan(int nchunk) {
+  if (nchunk == 896) return {7, 2, 3, true, true, 192};    // H = 7168
+  if (nchunk == 512) return {4, 2, 2, true, false, 256};   // H = 4096
+  return generic_plan(nchunk);
+}
+
+int64_t grid_of(const Plan& p, int64_t T) { return T < p.blocks ? T : p.blocks; }
+
+RowWalk row_walk(int64_t T, int64_t G) {
+  RowWalk w;
+  w.T = T;
+  w.block_stride = 1;
+  w.row_step = G > 0 ? G : 1;
+  w.per_block = G > 0 ? (T + G - 1) / G : 0;
+  return w;
 }
 
 template <class K>
@@ -508,17 +641,32 @@ struct FwdArgs {
   const f32x4 *wh, *we;
   u32x4* out;
   float* gate;
-  int64_t T;
+  RowWalk walk;
   int nchunk;
-  int64_t rpb;
   float eps, inv_h, inv_sqrt_h;
 };
 
-template <int W, int C, bool FULL>
+template <int W, int C, bool FULL, int D>
 tk_status run_fwd(FwdArgs a, int grid, hipStream_t st) {
-  void* args[] = {&a.x, &a.k, &a.v, &a.wh, &a.we, &a.out, &a.gate, &a.T,
-                  &a.nchunk, &a.rpb, &a.eps, &a.inv_h, &a.inv_sqrt_h};
-  return launch(gate_fwd_kernel<W, C, FULL>, grid, W * kWave, args, st);
+  void* args[] = {&a.x,    &a.k,      &a.v,   &a.wh,    &a.we,        &a.out,
+                  &a.gate, &a.walk, &a.nchunk, &a.eps, &a.inv_h, &a.inv_sqrt_h};
+  return launch(gate_fwd_kernel<W, C, FULL, D>, grid, W * kWave, args, st);
+}
+
+tk_status dispatch_fwd(const Plan& p, const FwdArgs& a, int grid, hipStream_t st) {
+  if (p.W == 7 && p.C == 2 && p.full && p.D == 3) return run_fwd<7, 2, true, 3>(a, grid, st);
+  if (p.W == 8 && p.C == 1 && p.full && p.D == 2) return run_fwd<8, 1, true, 2>(a, grid, st);
+  if (p.D == 2 && p.C == 1) {
+    switch (p.W) {
+      case 1: return run_fwd<1, 1, false, 2>(a, grid, st);
+      case 2: return run_fwd<2, 1, false, 2>(a, grid, st);
+      case 4: return run_fwd<4, 1, false, 2>(a, grid, st);
+      case 8: return run_fwd<8, 1, false, 2>(a, grid, st);
+      default: break;
+    }
+  }
+  if (p.W == 8 && p.C == 2 && p.D == 2) return run_fwd<8, 2, false, 2>(a, grid, st);
+  return TK_ERR_UNSUPPORTED;
 }
 
 struct BwdArgs {
@@ -526,39 +674,38 @@ struct BwdArgs {
   const f32x4 *wh, *we;
   u32x4 *dx, *dk, *dv;
   f32x4* partial;
-  int64_t T;
+  RowWalk walk;
   int nchunk;
-  int64_t rpb;
   float eps, clamp, inv_h, inv_sqrt_h;
 };
 
-template <int W, int C, bool FULL>
+template <int W, int C, bool FULL, int D, bool WLDS>
 tk_status run_bwd(BwdArgs a, int grid, hipStream_t st) {
-  void* args[] = {&a.g,  &a.x,       &a.k,      &a.v,   &a.wh,    &a.we,
-                  &a.dx, &a.dk,      &a.dv,     &a.partial, &a.T, &a.nchunk,
-                  &a.rpb, &a.eps,    &a.clamp,  &a.inv_h, &a.inv_sqrt_h};
-  return launch(gate_bwd_kernel<W, C, FULL>, grid, W * kWave, args, st);
+  void* args[] = {&a.g,       &a.x,    &a.k,      &a.v,   &a.wh,
+                  &a.we,      &a.dx,   &a.dk,     &a.dv,  &a.partial,
+                  &a.walk,    &a.nchunk, &a.eps,  &a.clamp, &a.inv_h,
+                  &a.inv_sqrt_h};
+  return launch(gate_bwd_kernel<W, C, FULL, D, WLDS>, grid, W * kWave, args, st);
 }
 
-// Dispatch over the instantiated shapes. Returns TK_ERR_UNSUPPORTED if the
-// shape picked does not cover the row (cannot happen for H <= 8192).
-#define TK_DISPATCH(RUN, ARGS, GRID, ST, SHAPE)                                 \
-  do {                                                                          \
-    const Shape s_ = (SHAPE);                                                   \
-    if (s_.W == 7 && s_.C == 2 && s_.full) return RUN<7, 2, true>(ARGS, GRID, ST); \
-    if (s_.W == 4 && s_.C == 2 && s_.full) return RUN<4, 2, true>(ARGS, GRID, ST); \
-    if (s_.C == 1) {                                                            \
-      switch (s_.W) {                                                           \
-        case 1: return RUN<1, 1, false>(ARGS, GRID, ST);                        \
-        case 2: return RUN<2, 1, false>(ARGS, GRID, ST);                        \
-        case 4: return RUN<4, 1, false>(ARGS, GRID, ST);                        \
-        case 8: return RUN<8, 1, false>(ARGS, GRID, ST);                        \
-        default: break;                                                         \
-      }                                                                         \
-    }                                                                           \
-    if (s_.W == 8 && s_.C == 2) return RUN<8, 2, false>(ARGS, GRID, ST);       \
-    return TK_ERR_UNSUPPORTED;                                                  \
-  } while (0)
+tk_status dispatch_bwd(const Plan& p, const BwdArgs& a, int grid, hipStream_t st) {
+  if (p.W == 7 && p.C == 2 && p.full && p.D == 3 && p.wlds)
+    return run_bwd<7, 2, true, 3, true>(a, grid, st);
+  if (p.W == 4 && p.C == 2 && p.full && p.D == 2 && !p.wlds)
+    return run_bwd<4, 2, true, 2, false>(a, grid, st);
+  if (p.D == 2 && !p.wlds && p.C == 1) {
+    switch (p.W) {
+      case 1: return run_bwd<1, 1, false, 2, false>(a, grid, st);
+      case 2: return run_bwd<2, 1, false, 2, false>(a, grid, st);
+      case 4: return run_bwd<4, 1, false, 2, false>(a, grid, st);
+      case 8: return run_bwd<8, 1, false, 2, false>(a, grid, st);
+      default: break;
+    }
+  }
+  if (p.W == 8 && p.C == 2 && p.D == 2 && !p.wlds)
+    return run_bwd<8, 2, false, 2, false>(a, grid, st);
+  return TK_ERR_UNSUPPORTED;
+}
 
 }  // namespace
 
@@ -582,12 +729,12 @@ const char* tk_status_string(tk_status s) {
 
 int64_t tk_engram_num_partials(int64_t T, int64_t H) {
   if (check_shape(T, H) != TK_SUCCESS) return 0;
-  return num_blocks(T);
+  return grid_of(bwd_plan((int)(H / 8)), T);
 }
 
 size_t tk_engram_bwd_workspace_bytes(int64_t T, int64_t H) {
   if (check_shape(T, H) != TK_SUCCESS) return 0;
-  return (size_t)num_blocks(T) * (size_t)H * sizeof(float);
+  return (size_t)tk_engram_num_partials(T, H) * (size_t)H * sizeof(float);
 }
 
 tk_status tk_engram_gate_fwd(const uint16_t* x, const uint16_t* k,
@@ -611,15 +758,14 @@ tk_status tk_engram_gate_fwd(const uint16_t* x, const uint16_t* k,
   a.we = reinterpret_cast<const f32x4*>(we);
   a.out = reinterpret_cast<u32x4*>(out);
   a.gate = gate;
-  a.T = T;
+  const Plan plan = fwd_plan(nchunk);
+  const int grid = (int)grid_of(plan, T);
+  a.walk = row_walk(T, grid);
   a.nchunk = nchunk;
-  a.rpb = rows_per_block(T);
   a.eps = (float)eps;
   a.inv_h = (float)(1.0 / (double)H);
   a.inv_sqrt_h = (float)(1.0 / std::sqrt((double)H));
-  const int grid = (int)num_blocks(T);
-  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-  TK_DISPATCH(run_fwd, a, grid, hs, pick_shape(nchunk));
+  return dispatch_fwd(plan, a, grid, reinterpret_cast<hipStream_t>(stream));
 }
 
 tk_status tk_engram_gate_bwd(const uint16_t* grad_out, const uint16_t* x,
@@ -651,16 +797,15 @@ tk_status tk_engram_gate_bwd(const uint16_t* grad_out, const uint16_t* x,
   a.dk = reinterpret_cast<u32x4*>(dk);
   a.dv = reinterpret_cast<u32x4*>(dv);
   a.partial = reinterpret_cast<f32x4*>(workspace);
-  a.T = T;
+  const Plan plan = bwd_plan(nchunk);
+  const int grid = (int)grid_of(plan, T);
+  a.walk = row_walk(T, grid);
   a.nchunk = nchunk;
-  a.rpb = rows_per_block(T);
   a.eps = (float)eps;
   a.clamp = (float)dsqrt_clamp;
   a.inv_h = (float)(1.0 / (double)H);
   a.inv_sqrt_h = (float)(1.0 / std::sqrt((double)H));
-  const int grid = (int)num_blocks(T);
-  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-  TK_DISPATCH(run_bwd, a, grid, hs, pick_shape(nchunk));
+  return dispatch_bwd(plan, a, grid, reinterpret_cast<hipStream_t>(stream));
 }
 
 tk_status tk_engram_grad_w_reduce(const float* workspace, int64_t P, int64_t H,
@@ -693,8 +838,8 @@ tk_status tk_engram_copy_probe(const void* src, void* dst, size_t bytes,
   const u32x4* s = reinterpret_cast<const u32x4*>(src);
   u32x4* d = reinterpret_cast<u32x4*>(dst);
   int64_t n = (int64_t)(bytes / 16);
-  int64_t blocks = (n + 255) / 256;
-  const int grid = (int)(blocks < 8192 ? blocks : 8192);
+  const int64_t tiles = (n + 256 * kCopyUnroll - 1) / (256 * kCopyUnroll);
+  const int grid = (int)(tiles < 16384 ? tiles : 16384);
   void* args[] = {&s, &d, &n};
   return launch(copy_probe_kernel, grid, 256, args,
                 reinterpret_cast<hipStream_t>(stream));

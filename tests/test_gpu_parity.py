@@ -213,7 +213,8 @@ def test_special_rows(eg, cuda_device):
         d["x"][2] = d["k"][2] = d["v"][2] = z    # everything zero
         d["v"][3] = z                            # no gradient reaches the gate
         d["x"][4] = d["k"][4]                    # k = x
-        d["k"][5] = d["x"][5] ^ 0x8000           # k = -x: mirrored gate
+        d["x"][5] = d["x"][4]                    # same x, k = -x: mirrored gate
+        d["k"][5] = d["x"][4] ^ 0x8000
         d["x"][6, 1::2] = 0                      # orthogonal supports: gate 1/2
         d["k"][6, 0::2] = 0
         big = oracle.round_bf16(oracle.bf16_to_f64(d["x"][7]) * 1e3)
@@ -232,7 +233,7 @@ def test_special_rows(eg, cuda_device):
     # v = 0: no gradient through the gate
     assert np.array_equal(g["dx"][3], d["grad_out"][3])
     assert np.all(oracle.bf16_to_f64(g["dk"][3]) == 0)
-    # mirrored gate
+    # mirrored gate: sigmoid(-s) = 1 - sigmoid(s)
     assert abs(gate[4] + gate[5] - 1.0) < 2e-6
 
 
