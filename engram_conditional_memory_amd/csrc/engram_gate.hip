@@ -72,18 +72,56 @@ __device__ __forceinline__ u32x4 pack8(const float f[8]) {
   return u;
 }
 
-// ---- wave reductions (xor butterfly: every lane ends with the same bits) ---
+// ---- wave reductions ---------------------------------------------------------
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int m = kWave / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
-  return v;
+// Sum over the 64 lanes of a wave, returned to every lane with the same bits.
+// Within each row of 16 lanes, four DPP steps combine lanes i^1, i^2 (quad
+// permutes), 7-i (half-row mirror) and 15-i (row mirror); IEEE addition is
+// commutative, so after each step all lanes of the group hold identical
+// values. The four row sums are then read from lanes 0, 16, 32 and 48 and
+// added in a fixed order. Everything stays in VALU/SALU, with none of the
+// LDS round trips of a permute-based butterfly.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
 }
 
-__device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-  for (int m = kWave / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
-  return v;
+constexpr int kDppXor1 = 0xB1;         // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;         // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141;  // row_half_mirror
+constexpr int kDppMirror = 0x140;      // row_mirror
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_step(float v) {
+  return v + __uint_as_float(dpp_u32<CTRL>(__float_as_uint(v)));
+}
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_step(double v) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint64_t lo = dpp_u32<CTRL>((uint32_t)u);
+  const uint64_t hi = dpp_u32<CTRL>((uint32_t)(u >> 32));
+  return v + __builtin_bit_cast(double, lo | (hi << 32));
+}
+
+__device__ __forceinline__ float lane_value(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+__device__ __forceinline__ double lane_value(double v, int lane) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint64_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, lane);
+  const uint64_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), lane);
+  return __builtin_bit_cast(double, lo | (hi << 32));
+}
+
+template <class F>
+__device__ __forceinline__ F wave_sum(F v) {
+  v = dpp_step<kDppXor1>(v);
+  v = dpp_step<kDppXor2>(v);
+  v = dpp_step<kDppHalfMirror>(v);
+  v = dpp_step<kDppMirror>(v);
+  return (lane_value(v, 0) + lane_value(v, 16)) + (lane_value(v, 32) + lane_value(v, 48));
 }
 
 // ---- per-thread slice of a row ---------------------------------------------
@@ -606,14 +644,16 @@ Plan generic_plan(int nchunk) {
   return {8, 2, 2, nchunk == 8 * kWave * 2, false, 256};
 }
 
+// The forward and the backward of one width split the row the same way (same
+// W and C), so the backward's recomputed gate has the forward's bits.
 Plan fwd_plan(int nchunk) {
-  if (nchunk == 896) return {7, 2, 3, true, false, 192};   // H = 7168
-  if (nchunk == 512) return {8, 1, 2, true, false, 256};   // H = 4096
+  if (nchunk == 896) return {7, 2, 2, true, false, 224};   // H = 7168
+  if (nchunk == 512) return {4, 2, 2, true, false, 256};   // H = 4096
   return generic_plan(nchunk);
 }
 
 Plan bwd_plan(int nchunk) {
-  if (nchunk == 896) return {7, 2, 3, true, true, 192};    // H = 7168
+  if (nchunk == 896) return {7, 2, 3, true, true, 224};    // H = 7168
   if (nchunk == 512) return {4, 2, 2, true, false, 256};   // H = 4096
   return generic_plan(nchunk);
 }
@@ -654,8 +694,8 @@ tk_status run_fwd(FwdArgs a, int grid, hipStream_t st) {
 }
 
 tk_status dispatch_fwd(const Plan& p, const FwdArgs& a, int grid, hipStream_t st) {
-  if (p.W == 7 && p.C == 2 && p.full && p.D == 3) return run_fwd<7, 2, true, 3>(a, grid, st);
-  if (p.W == 8 && p.C == 1 && p.full && p.D == 2) return run_fwd<8, 1, true, 2>(a, grid, st);
+  if (p.W == 7 && p.C == 2 && p.full && p.D == 2) return run_fwd<7, 2, true, 2>(a, grid, st);
+  if (p.W == 4 && p.C == 2 && p.full && p.D == 2) return run_fwd<4, 2, true, 2>(a, grid, st);
   if (p.D == 2 && p.C == 1) {
     switch (p.W) {
       case 1: return run_fwd<1, 1, false, 2>(a, grid, st);

@@ -113,7 +113,9 @@ size_t tk_engram_bwd_workspace_bytes(int64_t T, int64_t H);
  *                     stays finite at z = 0 (the page gives no value there);
  *                     finite and > 0
  *
- * The gate is recomputed from x and k exactly as the forward computes it.
+ * The gate is recomputed from x and k with the forward's arithmetic and
+ * summation order, so it has the forward's bits and dv = bf16(gate * grad_out)
+ * with the forward's fp32 gate.
  */
 tk_status tk_engram_gate_bwd(const uint16_t* grad_out, const uint16_t* x,
                              const uint16_t* k, const uint16_t* v,

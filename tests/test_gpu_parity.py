@@ -123,6 +123,19 @@ def compare(d, g, backward=True, chunk=2048):
     return rep
 
 
+def assert_dv_is_gate_times_grad(d, g, chunk=4096):
+    """The backward recomputes the forward's gate bit for bit, so dv must be
+    the fp32 product gate * grad_out (gate from the forward) rounded once to
+    bf16, element for element."""
+    T = d["x"].shape[0]
+    for a in range(0, T, chunk):
+        sl = slice(a, min(T, a + chunk))
+        gout = oracle.bf16_to_f64(d["grad_out"][sl]).astype(np.float32)
+        prod = g["gate"][sl].astype(np.float32)[:, None] * gout      # fp32 multiply
+        want = oracle.round_bf16(prod.astype(np.float64))
+        assert np.array_equal(g["dv"][sl], want), f"dv rows {sl}"
+
+
 def assert_report(rep, backward=True, name=""):
     out = rep["out"]
     say(f"[{name}] gate max err {rep['gate_err']:.3e} (min |z| {rep['min_abs_z']:.2e}); "
@@ -149,6 +162,7 @@ def test_config1_tiny(eg, cuda_device):
     g = run_gpu(eg, d, cuda_device)
     rep = compare(d, g)
     assert_report(rep, name="tiny T=64 H=256")
+    assert_dv_is_gate_times_grad(d, g)
     # the tiny workload is small enough for a strict elementwise check too
     assert rep["st"]["dv"].max_ulp() <= 1
 
@@ -168,6 +182,7 @@ def test_full_size(eg, cuda_device, cfg):
     g = run_gpu(eg, d, cuda_device)
     say(f"[config {cfg}] GPU done (P={g['P']}), comparing with the oracle")
     assert_report(compare(d, g), name=c.name)
+    assert_dv_is_gate_times_grad(d, g)
 
 
 # ------------------------------------------------------------- determinism
@@ -201,6 +216,7 @@ def test_shapes(eg, cuda_device, T, H):
     d = make_case(T, H, seed=T * 7 + H)
     g = run_gpu(eg, d, cuda_device)
     assert_report(compare(d, g), name=f"T={T} H={H}")
+    assert_dv_is_gate_times_grad(d, g)
 
 
 def test_special_rows(eg, cuda_device):
