@@ -28,3 +28,14 @@ from ._binding import (  # noqa: F401
     tk_status_string,
 )
 from .build import LIB as LIBRARY_PATH  # noqa: F401
+
+# The autograd wrapper imports torch; load it on first use.
+_AUTOGRAD = ("EngramGateFunction", "EngramGate", "engram_gate")
+
+
+def __getattr__(name):
+    if name in _AUTOGRAD:
+        from . import autograd
+        return getattr(autograd, name)
+    raise AttributeError(f"module {__name__!r} has no attribute {name!r}")
+

@@ -7,6 +7,7 @@ links or calls it, and it imports nothing from the GPU library.
 What it computes is the gate of the zhichai.net TileKernels page, section
 "5. Engram" (gate formula), and its chain-rule backward; the readings taken
 where that page is silent are listed at the top of ``engram_oracle.cpp``.
+The same section's N-gram hash (engram_hash) is in ``engram_hash_oracle.cpp``.
 """
 
 from __future__ import annotations
@@ -20,6 +21,7 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "engram_oracle.cpp")
 _SRC_CMP = os.path.join(_HERE, "compare.cpp")
+_SRC_HASH = os.path.join(_HERE, "engram_hash_oracle.cpp")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
 EPS = 1e-6          # RMSNorm epsilon used throughout (the pages give none)
@@ -29,7 +31,7 @@ CLAMP = 1e-4        # lower clamp of |z| in the signed-sqrt derivative
 def build(verbose: bool = False) -> str:
     """Compile the oracle with g++ (no fast-math, no FMA contraction)."""
     cmd = ["g++", "-O2", "-std=c++17", "-ffp-contract=off", "-fPIC", "-shared",
-           "-pthread", _SRC, _SRC_CMP, "-o", _LIB]
+           "-pthread", _SRC, _SRC_CMP, _SRC_HASH, "-o", _LIB]
     if verbose:
         print(" ".join(cmd))
     subprocess.run(cmd, check=True)
@@ -55,9 +57,11 @@ def lib() -> ctypes.CDLL:
         L.oracle_round_bf16.argtypes = [vp, i64, vp]
         L.oracle_compare_bf16.argtypes = [vp, vp, i64, i64, vp, vp, i32]
         L.oracle_check_out.argtypes = [vp, vp, vp, vp, vp, i64, i64, vp, i32]
+        L.oracle_engram_hash.argtypes = [vp, i64, i64, i32, i32, vp, vp, vp,
+                                         ctypes.c_uint32, vp]
         for n in ("oracle_fwd_f64", "oracle_bwd_f64", "oracle_fwd_bf16",
                   "oracle_bwd_bf16", "oracle_round_bf16", "oracle_compare_bf16",
-                  "oracle_check_out"):
+                  "oracle_check_out", "oracle_engram_hash"):
             getattr(L, n).restype = None
         L.oracle_fwd_stats_width.restype = i32
         L.oracle_bwd_stats_width.restype = i32
@@ -206,3 +210,27 @@ def check_out(gpu_bits, ref, x_bits, v_bits, gate, res=None, threads=None):
     lib().oracle_check_out(_p(arrs[0]), _p(ref), _p(arrs[1]), _p(arrs[2]), _p(gate),
                            rows, H, _p(res), threads or default_threads())
     return res
+
+
+# ---- N-gram hash (engram_hash_oracle.cpp) -------------------------------------
+
+def engram_hash(tokens, ngram, mult, table_size, pad):
+    """Table indices int32 [B, S, L, K] of the N-gram hash.
+
+    tokens int32 [B, S]; ngram [L] N-gram orders (1..4); mult uint64 [L, K, 4]
+    multipliers (entries past n_l unused); table_size uint32 [L, K]; pad the
+    token id read before the start of a sequence."""
+    tokens = np.ascontiguousarray(tokens, dtype=np.int32)
+    assert tokens.ndim == 2
+    B, S = tokens.shape
+    ngram = np.ascontiguousarray(ngram, dtype=np.int32)
+    mult = np.ascontiguousarray(mult, dtype=np.uint64)
+    table_size = np.ascontiguousarray(table_size, dtype=np.uint32)
+    L, K = table_size.shape
+    assert ngram.shape == (L,) and mult.shape == (L, K, 4)
+    assert np.all((ngram >= 1) & (ngram <= 4)) and np.all(table_size >= 1)
+    out = np.empty((B, S, L, K), dtype=np.int32)
+    lib().oracle_engram_hash(_p(tokens), B, S, L, K, _p(ngram), _p(mult), _p(table_size),
+                             int(pad) & 0xFFFFFFFF, _p(out))
+    return out
+

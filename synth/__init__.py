@@ -30,6 +30,7 @@ STREAM_X, STREAM_K, STREAM_V, STREAM_GOUT = 1, 2, 3, 4
 STREAM_WH, STREAM_WE = 5, 6
 STREAM_RHO, STREAM_KNOISE = 7, 8
 STREAM_MASK = {"x": 9, "k": 10, "v": 11}
+STREAM_TOKENS = 12
 
 
 def build(verbose: bool = False) -> str:
@@ -215,3 +216,88 @@ def make_inputs(cfg: int | Config, seed: int = 0, rows: tuple[int, int] | None =
     if with_grad:
         out["grad_out"] = normal_bf16(seed, STREAM_GOUT, (n, H), e0=e0, threads=th)
     return out
+
+
+# ---- N-gram hash workloads ---------------------------------------------------
+
+_MASK64 = (1 << 64) - 1
+
+
+def splitmix64(seed: int, n: int) -> list:
+    """n outputs of SplitMix64 (Steele, Lea and Flood, OOPSLA 2014) from `seed`."""
+    out = []
+    state = seed & _MASK64
+    for _ in range(n):
+        state = (state + 0x9E3779B97F4A7C15) & _MASK64
+        z = state
+        z = ((z ^ (z >> 30)) * 0xBF58476D1CE4E5B9) & _MASK64
+        z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & _MASK64
+        out.append(z ^ (z >> 31))
+    return out
+
+
+def _is_prime(n: int) -> bool:
+    if n < 2:
+        return False
+    if n % 2 == 0:
+        return n == 2
+    f = 3
+    while f * f <= n:
+        if n % f == 0:
+            return False
+        f += 2
+    return True
+
+
+def primes_below(limit: int, count: int) -> list:
+    """The `count` largest primes below `limit`, descending."""
+    out = []
+    n = limit - 1
+    while len(out) < count:
+        if _is_prime(n):
+            out.append(n)
+        n -= 1
+    return out
+
+
+@dataclass(frozen=True)
+class HashConfig:
+    name: str
+    B: int
+    S: int
+    ngram: tuple         # N-gram order of each layer
+    tables: int          # tables per layer
+    table_rows: int      # table sizes are distinct primes just below this
+    vocab: int
+    describe: str
+
+
+HASH_CONFIGS = {
+    "tiny": HashConfig("hash_tiny", 3, 37, (2, 3), 8, 1021, 1000,
+                       "3 sequences of 37 tokens, 2-gram and 3-gram layers, 8 tables each"),
+    "b8s4096": HashConfig("hash_b8s4096", 8, 4096, (2, 3), 8, 1 << 19, 129280,
+                          "batch 8 x seq 4096 = 32768 tokens (the H=7168 gate workload), "
+                          "2-gram and 3-gram layers, 8 tables each of ~2^19 rows"),
+    "b64s4096": HashConfig("hash_b64s4096", 64, 4096, (2, 3), 8, 1 << 19, 129280,
+                           "batch 64 x seq 4096 = 262144 tokens, same layers and tables"),
+}
+
+
+def hash_params(cfg: HashConfig, seed: int = 0) -> dict:
+    """Multipliers (odd, SplitMix64 from the seed) and prime table sizes for a
+    hash workload; the pad id is the vocabulary size (one past the last id)."""
+    L, K = len(cfg.ngram), cfg.tables
+    raw = splitmix64(seed ^ 0x5EEDBA5E, L * K * 4)
+    mult = np.array([v | 1 for v in raw], dtype=np.uint64).reshape(L, K, 4)
+    sizes = np.array(primes_below(cfg.table_rows, L * K), dtype=np.uint32).reshape(L, K)
+    return {"ngram": np.array(cfg.ngram, dtype=np.int32), "mult": mult,
+            "table_size": sizes, "pad": cfg.vocab}
+
+
+def hash_tokens(cfg: HashConfig, seed: int = 0) -> np.ndarray:
+    """Token ids int32 [B, S], uniform over the vocabulary (Philox stream)."""
+    n = cfg.B * cfg.S
+    u = uniform_pm1(seed, STREAM_TOKENS, n)          # in [-1, 1)
+    ids = np.floor((u + 1.0) * 0.5 * cfg.vocab).astype(np.int64)
+    return np.clip(ids, 0, cfg.vocab - 1).astype(np.int32).reshape(cfg.B, cfg.S)
+

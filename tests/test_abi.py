@@ -159,3 +159,13 @@ def test_product_path_does_not_touch_the_oracle():
                 assert "oracle" not in text.lower(), f
     with open(eg.LIBRARY_PATH, "rb") as fh:
         assert b"oracle_" not in fh.read()
+
+
+def test_autograd_wrapper_rejects_host_tensors():
+    # the gate has no CPU implementation: host tensors are refused before any
+    # library call
+    import torch
+    m = eg.EngramGate(64)
+    x = torch.zeros(3, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        m(x, x, x)
