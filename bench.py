@@ -152,6 +152,30 @@ def time_workload(w: Workload, steps: int, warmup: int) -> dict:
     }
 
 
+def time_hash(eg, dev, name: str = "b1024s4096", reps: int = 20) -> dict:
+    """tk_engram_hash throughput on a large batch: average launch time from HIP
+    events over back-to-back launches; algorithmic bytes = 4 per token read
+    plus 4 per index written."""
+    import synth
+    import torch
+    c = synth.HASH_CONFIGS[name]
+    p = synth.hash_params(c)
+    tokens = torch.from_numpy(synth.hash_tokens(c)).to(dev)
+    out = torch.empty((c.B, c.S, len(c.ngram), c.tables), dtype=torch.int32, device=dev)
+
+    def call():
+        eg.tk_engram_hash(tokens, p["ngram"], p["mult"], p["table_size"], p["pad"], out)
+
+    us = avg_launch_us(call, reps)
+    n = c.B * c.S
+    nbytes = n * (4 + 4 * len(c.ngram) * c.tables)
+    del tokens, out
+    torch.cuda.empty_cache()
+    return {"workload": c.name, "tokens": n, "us": us, "tokens_per_s": n / (us / 1e6),
+            "bytes": nbytes, "GBps": nbytes / (us * 1e3),
+            "frac": nbytes / (us * 1e3) / HBM_PEAK_GBPS}
+
+
 def copy_ceiling(nbytes: int, eg, dev, reps: int = 20) -> dict:
     import torch
     src = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=dev).fill_(1.0)
@@ -308,6 +332,8 @@ def main():
         torch.cuda.empty_cache()
 
     copy = copy_ceiling(2 * main_res["T"] * main_res["H"], eg, dev)
+    print("[bench] timing the N-gram hash", file=sys.stderr, flush=True)
+    hash_res = time_hash(eg, dev)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -341,6 +367,7 @@ def main():
         "reduce_us": main_res["reduce_us"],
         "secondary": secondary,
         "copy_probe": copy,
+        "hash": hash_res,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line))

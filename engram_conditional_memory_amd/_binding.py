@@ -29,8 +29,10 @@ TK_ERR_VALUE = 7
 EXPORTS = (
     "tk_engram_gate_fwd", "tk_engram_gate_bwd", "tk_engram_grad_w_reduce",
     "tk_engram_num_partials", "tk_engram_bwd_workspace_bytes",
-    "tk_engram_copy_probe", "tk_status_string", "tk_abi_version",
+    "tk_engram_copy_probe", "tk_status_string", "tk_abi_version", "tk_engram_hash",
 )
+
+HASH_MAX_NGRAM = 4
 
 
 class TkError(RuntimeError):
@@ -71,6 +73,8 @@ def load_library(path: str = LIB) -> ctypes.CDLL:
     L.tk_status_string.restype = ctypes.c_char_p
     L.tk_abi_version.argtypes = []
     L.tk_abi_version.restype = i32
+    L.tk_engram_hash.argtypes = [vp, i64, i64, i32, i32, vp, vp, vp, ctypes.c_uint32, vp, vp]
+    L.tk_engram_hash.restype = i32
     _lib = L
     return L
 
@@ -281,3 +285,44 @@ def bind_grad_w_reduce(workspace, P, H, wh, we, dwh, dwe, stream=None):
             _stream_handle(dev, stream)]
     return BoundCall("tk_engram_grad_w_reduce", load_library().tk_engram_grad_w_reduce,
                      args, (workspace, wh, we, dwh, dwe))
+
+
+# ---- N-gram hash --------------------------------------------------------------
+
+def _host_array(a, dtype, shape, name):
+    import numpy as np
+    a = np.ascontiguousarray(a, dtype=dtype)
+    if a.shape != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {a.shape}")
+    return a
+
+
+def tk_engram_hash(tokens, ngram, mult, table_size, pad, out=None, stream=None):
+    """Table indices int32 [B, S, L, K] of the N-gram hash of `tokens` (int32
+    [B, S] on the GPU). ngram [L], mult uint64 [L, K, 4] and table_size uint32
+    [L, K] are host arrays (numpy or lists)."""
+    import numpy as np
+    torch = _torch()
+    if not isinstance(tokens, torch.Tensor) or tokens.dim() != 2:
+        raise ValueError("tokens must be a 2-D [B, S] tensor")
+    if tokens.device.type != "cuda":
+        raise ValueError("tokens must be a GPU tensor")
+    B, S = tokens.shape
+    dev = tokens.device
+    table_size = np.ascontiguousarray(table_size, dtype=np.uint32)
+    if table_size.ndim != 2:
+        raise ValueError("table_size must be [L, K]")
+    L, K = table_size.shape
+    ngram = _host_array(ngram, np.int32, (L,), "ngram")
+    mult = _host_array(mult, np.uint64, (L, K, HASH_MAX_NGRAM), "mult")
+    if out is None:
+        out = torch.empty((B, S, L, K), dtype=torch.int32, device=dev)
+    tp = _need(tokens, "tokens", torch.int32, (B, S), dev)
+    op = _need(out, "out", torch.int32, (B, S, L, K), dev)
+    st = load_library().tk_engram_hash(
+        tp, B, S, L, K, ctypes.c_void_p(ngram.ctypes.data), ctypes.c_void_p(mult.ctypes.data),
+        ctypes.c_void_p(table_size.ctypes.data), int(pad) & 0xFFFFFFFF, op,
+        _stream_handle(dev, stream))
+    _check("tk_engram_hash", st)
+    return out
+

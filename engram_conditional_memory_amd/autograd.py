@@ -44,8 +44,9 @@ class EngramGateFunction(torch.autograd.Function):
         out, gate = B.tk_engram_gate_fwd(x2, k2, v2, wh_c, we_c, eps=eps)
         ctx.save_for_backward(x2, k2, v2, wh_c, we_c)
         ctx.eps, ctx.clamp, ctx.lead, ctx.H = eps, dsqrt_clamp, lead, H
+        gate = gate.view(lead)
         ctx.mark_non_differentiable(gate)
-        return out.view(*lead, H), gate.view(lead)
+        return out.view(*lead, H), gate
 
     @staticmethod
     def backward(ctx, grad_out, grad_gate):

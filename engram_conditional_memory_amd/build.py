@@ -7,7 +7,8 @@ import subprocess
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "engram_gate.hip")
+SRCS = [os.path.join(PKG, "csrc", "engram_gate.hip"),
+        os.path.join(PKG, "csrc", "engram_hash.hip")]
 LIB = os.path.join(PKG, "libtk_engram.so")
 INCLUDE = os.path.join(ROOT, "include")
 
@@ -17,7 +18,7 @@ def hipcc_command(out: str = LIB) -> list[str]:
         "hipcc", "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
         # packed fp32 instructions stay off on this device
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-        "-I", INCLUDE, SRC, "-o", out,
+        "-I", INCLUDE, *SRCS, "-o", out,
     ]
 
 

@@ -762,7 +762,7 @@ const char* tk_status_string(tk_status s) {
     case TK_ERR_UNSUPPORTED: return "H exceeds the supported maximum (8192)";
     case TK_ERR_WORKSPACE: return "backward workspace is smaller than required";
     case TK_ERR_LAUNCH: return "kernel launch failed";
-    case TK_ERR_VALUE: return "eps or clamp is not a finite positive number";
+    case TK_ERR_VALUE: return "a scalar or table parameter is out of range";
     default: return "unknown status";
   }
 }

@@ -62,7 +62,7 @@ enum {
   TK_ERR_UNSUPPORTED = 4, /* H above the supported maximum                  */
   TK_ERR_WORKSPACE = 5,   /* backward workspace smaller than required       */
   TK_ERR_LAUNCH = 6,      /* the HIP runtime refused the kernel launch      */
-  TK_ERR_VALUE = 7        /* eps or clamp not a finite positive number      */
+  TK_ERR_VALUE = 7        /* a scalar or table parameter is out of range    */
 };
 
 #define TK_ENGRAM_ABI_VERSION 1
@@ -140,6 +140,42 @@ tk_status tk_engram_gate_bwd(const uint16_t* grad_out, const uint16_t* x,
 tk_status tk_engram_grad_w_reduce(const float* workspace, int64_t P, int64_t H,
                                   const float* wh, const float* we, float* dwh,
                                   float* dwe, void* stream);
+
+/*
+ * N-gram hash of the Engram memory (section "5. Engram": engram_hash, the
+ * step before the gate: N-gram token ids combined by XOR and multiplication
+ * and mapped to embedding-table indices; the page describes 2 N-gram layers,
+ * N up to 3, and 8 tables per layer). The page gives no constants, so the
+ * multipliers and table sizes are the caller's. For sequence b, position s,
+ * layer l and table j of that layer:
+ *
+ *   h   = XOR over i < ngram[l] of ( tok(b, s - i) * mult[l][j][i]  mod 2^64 )
+ *   out[b][s][l][j] = h mod table_size[l][j]
+ *
+ * where tok(b, p) is tokens[b][p] taken as an unsigned 32-bit pattern, and
+ * `pad` for p < 0 (before the start of the sequence).
+ *
+ *   tokens     : int32 [B, S], device, 4-byte aligned
+ *   ngram      : int32 [L], HOST, each in 1 .. TK_ENGRAM_HASH_MAX_NGRAM
+ *   mult       : uint64 [L, K, TK_ENGRAM_HASH_MAX_NGRAM], HOST (entries
+ *                i >= ngram[l] are ignored)
+ *   table_size : uint32 [L, K], HOST, each in 1 .. TK_ENGRAM_HASH_MAX_TABLE_SIZE
+ *   out        : int32 [B, S, L, K], device, 16-byte aligned
+ *
+ * Limits: L, K >= 1, L * K <= TK_ENGRAM_HASH_MAX_TABLES, B <=
+ * TK_ENGRAM_HASH_MAX_BATCH. The host arrays are read during the call only.
+ * B = 0 or S = 0 is a successful no-op. Exact integer arithmetic: results are
+ * bit-identical to any correct implementation of the formula above.
+ */
+#define TK_ENGRAM_HASH_MAX_TABLES 32
+#define TK_ENGRAM_HASH_MAX_NGRAM 4
+#define TK_ENGRAM_HASH_MAX_TABLE_SIZE 2147483648u
+#define TK_ENGRAM_HASH_MAX_BATCH 65535
+
+tk_status tk_engram_hash(const int32_t* tokens, int64_t B, int64_t S, int32_t L,
+                         int32_t K, const int32_t* ngram, const uint64_t* mult,
+                         const uint32_t* table_size, uint32_t pad, int32_t* out,
+                         void* stream);
 
 /*
  * Measurement aid, not part of the gate: copies `bytes` bytes (a multiple

@@ -280,6 +280,9 @@ HASH_CONFIGS = {
                           "2-gram and 3-gram layers, 8 tables each of ~2^19 rows"),
     "b64s4096": HashConfig("hash_b64s4096", 64, 4096, (2, 3), 8, 1 << 19, 129280,
                            "batch 64 x seq 4096 = 262144 tokens, same layers and tables"),
+    "b1024s4096": HashConfig("hash_b1024s4096", 1024, 4096, (2, 3), 8, 1 << 19, 129280,
+                             "batch 1024 x seq 4096 = 4194304 tokens (throughput), "
+                             "same layers and tables"),
 }
 
 

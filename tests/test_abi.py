@@ -169,3 +169,37 @@ def test_autograd_wrapper_rejects_host_tensors():
     x = torch.zeros(3, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="GPU tensor"):
         m(x, x, x)
+
+
+def hsh(**kw):
+    import numpy as np
+    a = dict(tokens=A16, B=2, S=5, L=2, K=8, ngram=[2, 3], table=None, pad=0, out=A16)
+    a.update(kw)
+    L, K = a["L"], a["K"]
+    ngram = np.ascontiguousarray(a["ngram"], dtype=np.int32)
+    mult = np.ones((max(L, 1), max(K, 1), 4), dtype=np.uint64)
+    table = (np.full((max(L, 1), max(K, 1)), 1021, dtype=np.uint32) if a["table"] is None
+             else np.ascontiguousarray(a["table"], dtype=np.uint32))
+    return eg.load_library().tk_engram_hash(
+        a["tokens"], a["B"], a["S"], L, K, ngram.ctypes.data, mult.ctypes.data,
+        table.ctypes.data, a["pad"], a["out"], None)
+
+
+def test_hash_argument_checks():
+    assert hsh(B=-1) == B.TK_ERR_SHAPE
+    assert hsh(L=0, ngram=[2]) == B.TK_ERR_SHAPE
+    assert hsh(K=0) == B.TK_ERR_SHAPE
+    assert hsh(L=2, K=17) == B.TK_ERR_UNSUPPORTED           # 34 tables
+    assert hsh(B=65536) == B.TK_ERR_UNSUPPORTED
+    assert hsh(ngram=[2, 5]) == B.TK_ERR_VALUE
+    assert hsh(ngram=[0, 3]) == B.TK_ERR_VALUE
+    t = [[1021] * 8, [1021] * 7 + [0]]
+    assert hsh(table=t) == B.TK_ERR_VALUE
+    t = [[1021] * 8, [1021] * 7 + [(1 << 31) + 1]]
+    assert hsh(table=t) == B.TK_ERR_VALUE
+    assert hsh(B=0, tokens=None, out=None) == B.TK_SUCCESS
+    assert hsh(S=0, tokens=None, out=None) == B.TK_SUCCESS
+    assert hsh(tokens=None) == B.TK_ERR_NULL
+    assert hsh(out=None) == B.TK_ERR_NULL
+    assert hsh(tokens=A16 + 2) == B.TK_ERR_ALIGN
+    assert hsh(out=A16 + 4) == B.TK_ERR_ALIGN
