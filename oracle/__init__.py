@@ -234,3 +234,19 @@ def engram_hash(tokens, ngram, mult, table_size, pad):
                              int(pad) & 0xFFFFFFFF, _p(out))
     return out
 
+
+# ---- hashed multi-table gather ---------------------------------------------------
+
+def engram_gather(idx, table_data, row_offset, rows):
+    """out [T, Q, d] with out[t, q] = table_data[row_offset[q] + idx[t, q]] when
+    0 <= idx[t, q] < rows[q], else a zero row (bf16 bit patterns)."""
+    idx = np.asarray(idx, dtype=np.int64)
+    T, Q = idx.shape
+    row_offset = np.asarray(row_offset, dtype=np.int64)
+    rows = np.asarray(rows, dtype=np.int64)
+    valid = (idx >= 0) & (idx < rows[None, :])
+    src = np.where(valid, row_offset[None, :] + idx, 0)
+    out = table_data[src]                       # library gather
+    out[~valid] = 0
+    return out
+

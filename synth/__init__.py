@@ -304,3 +304,58 @@ def hash_tokens(cfg: HashConfig, seed: int = 0) -> np.ndarray:
     ids = np.floor((u + 1.0) * 0.5 * cfg.vocab).astype(np.int64)
     return np.clip(ids, 0, cfg.vocab - 1).astype(np.int32).reshape(cfg.B, cfg.S)
 
+
+# ---- embedding tables for the hashed gather -----------------------------------
+
+def table_bits_np(q: int, rows, d: int) -> np.ndarray:
+    """bf16 bit patterns of rows `rows` (int array) of table q, [len(rows), d].
+
+    Each value is a finite bf16 in +-[1, 2) whose bits come from an integer
+    mix of (table, row, column), so every row of every table is distinct and
+    can be recomputed anywhere from its coordinates."""
+    rows = np.asarray(rows, dtype=np.uint64).reshape(-1, 1)
+    cols = np.arange(d, dtype=np.uint64).reshape(1, -1)
+    h = (rows * np.uint64(0x9E3779B1) + cols * np.uint64(0x85EBCA77)
+         + np.uint64(q) * np.uint64(0xC2B2AE3D)) & np.uint64(0xFFFFFFFF)
+    h ^= h >> np.uint64(15)
+    h = (h * np.uint64(0x2C1B3C6D)) & np.uint64(0xFFFFFFFF)
+    h ^= h >> np.uint64(12)
+    sign = (h >> np.uint64(20)) & np.uint64(1)
+    return ((sign << np.uint64(15)) | np.uint64(0x3F80) | (h & np.uint64(0x7F))).astype(np.uint16)
+
+
+def fill_table_bits_torch(data, q: int, row0: int, rows: int, d: int):
+    """The same pattern as table_bits_np, written into rows [row0, row0 + rows)
+    of the bf16 tensor `data` [R, d] with torch integer ops on its device."""
+    import torch
+    dev = data.device
+    r = torch.arange(rows, dtype=torch.int64, device=dev).view(-1, 1)
+    c = torch.arange(d, dtype=torch.int64, device=dev).view(1, -1)
+    m32 = 0xFFFFFFFF
+    h = (r * 0x9E3779B1 + c * 0x85EBCA77 + q * 0xC2B2AE3D) & m32
+    h = h ^ (h >> 15)
+    h = (h * 0x2C1B3C6D) & m32
+    h = h ^ (h >> 12)
+    bits = (((h >> 20) & 1) << 15) | 0x3F80 | (h & 0x7F)
+    bits = torch.where(bits >= 0x8000, bits - 0x10000, bits).to(torch.int16)
+    data[row0:row0 + rows].view(torch.int16).copy_(bits)
+
+
+@dataclass(frozen=True)
+class GatherConfig:
+    name: str
+    T: int
+    tables: int
+    rows: int            # rows per table
+    d: int               # row width (bf16)
+    describe: str
+
+
+GATHER_CONFIGS = {
+    "tiny": GatherConfig("gather_tiny", 40, 16, 1021, 24,
+                         "40 tokens x 16 tables of 1021 rows x 24"),
+    "t32768_d448": GatherConfig("gather_t32768_d448", 32768, 16, 1 << 19, 448,
+                                "32768 tokens x 16 tables (2 layers x 8) of 2^19 rows x 448 "
+                                "bf16 (16 x 448 = 7168 = H)"),
+}
+
