@@ -176,6 +176,40 @@ def time_hash(eg, dev, name: str = "b1024s4096", reps: int = 20) -> dict:
             "frac": nbytes / (us * 1e3) / HBM_PEAK_GBPS}
 
 
+def time_gather(eg, dev, reps: int = 20) -> dict:
+    """tk_engram_gather on the H=7168 workload's memory read: 32768 tokens, 16
+    tables (2 layers x 8) of 2^19 rows x 448 bf16, indices from
+    tk_engram_hash. Algorithmic bytes per (token, table): 4 (index) + 2d
+    (row read) + 2d (row written)."""
+    import synth
+    import torch
+    hc = synth.HASH_CONFIGS["b8s4096"]
+    gc = synth.GATHER_CONFIGS["t32768_d448"]
+    p = synth.hash_params(hc)
+    stride = 1 << 19
+    data = torch.empty((gc.tables * stride, gc.d), dtype=torch.bfloat16, device=dev)
+    for q in range(gc.tables):
+        synth.fill_table_bits_torch(data, q, q * stride, stride, gc.d)
+    off = np.arange(gc.tables, dtype=np.int64) * stride
+    sizes = p["table_size"].reshape(-1)
+    tokens = torch.from_numpy(synth.hash_tokens(hc)).to(dev)
+    idx = eg.tk_engram_hash(tokens, p["ngram"], p["mult"], p["table_size"], p["pad"])
+    out = torch.empty((gc.T, gc.tables, gc.d), dtype=torch.bfloat16, device=dev)
+    idx2 = idx.view(gc.T, gc.tables)
+
+    def call():
+        eg.tk_engram_gather(idx2, data, off, sizes, out)
+
+    us = avg_launch_us(call, reps)
+    n = gc.T * gc.tables
+    nbytes = n * (4 + 4 * gc.d)
+    del data, tokens, idx, out, idx2
+    torch.cuda.empty_cache()
+    return {"workload": gc.name, "tokens": gc.T, "rows_gathered": n, "us": us,
+            "tokens_per_s": gc.T / (us / 1e6), "bytes": nbytes,
+            "GBps": nbytes / (us * 1e3), "frac": nbytes / (us * 1e3) / HBM_PEAK_GBPS}
+
+
 def copy_ceiling(nbytes: int, eg, dev, reps: int = 20) -> dict:
     import torch
     src = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=dev).fill_(1.0)
@@ -334,6 +368,8 @@ def main():
     copy = copy_ceiling(2 * main_res["T"] * main_res["H"], eg, dev)
     print("[bench] timing the N-gram hash", file=sys.stderr, flush=True)
     hash_res = time_hash(eg, dev)
+    print("[bench] timing the hashed gather", file=sys.stderr, flush=True)
+    gather_res = time_gather(eg, dev)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -368,6 +404,7 @@ def main():
         "secondary": secondary,
         "copy_probe": copy,
         "hash": hash_res,
+        "gather": gather_res,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line))

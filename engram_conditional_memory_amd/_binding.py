@@ -30,6 +30,7 @@ EXPORTS = (
     "tk_engram_gate_fwd", "tk_engram_gate_bwd", "tk_engram_grad_w_reduce",
     "tk_engram_num_partials", "tk_engram_bwd_workspace_bytes",
     "tk_engram_copy_probe", "tk_status_string", "tk_abi_version", "tk_engram_hash",
+    "tk_engram_gather",
 )
 
 HASH_MAX_NGRAM = 4
@@ -75,6 +76,8 @@ def load_library(path: str = LIB) -> ctypes.CDLL:
     L.tk_abi_version.restype = i32
     L.tk_engram_hash.argtypes = [vp, i64, i64, i32, i32, vp, vp, vp, ctypes.c_uint32, vp, vp]
     L.tk_engram_hash.restype = i32
+    L.tk_engram_gather.argtypes = [vp, i64, i32, vp, i64, i64, vp, vp, vp, vp]
+    L.tk_engram_gather.restype = i32
     _lib = L
     return L
 
@@ -324,5 +327,38 @@ def tk_engram_hash(tokens, ngram, mult, table_size, pad, out=None, stream=None):
         ctypes.c_void_p(table_size.ctypes.data), int(pad) & 0xFFFFFFFF, op,
         _stream_handle(dev, stream))
     _check("tk_engram_hash", st)
+    return out
+
+
+# ---- hashed multi-table gather ---------------------------------------------------
+
+def tk_engram_gather(idx, table_data, row_offset, rows, out=None, stream=None):
+    """out [T, Q, d] bf16: row row_offset[q] + idx[t, q] of `table_data` (bf16
+    [R, d] on the GPU) for every token t and table q; a zero row where the
+    index is outside table q. idx is int32 [T, Q] (or [..., Q], flattened) on
+    the GPU; row_offset (int64) and rows (uint32) are host arrays of length Q."""
+    import numpy as np
+    torch = _torch()
+    if not isinstance(idx, torch.Tensor) or idx.dim() < 1 or idx.device.type != "cuda":
+        raise ValueError("idx must be an int32 GPU tensor [..., Q]")
+    if not isinstance(table_data, torch.Tensor) or table_data.dim() != 2:
+        raise ValueError("table_data must be a 2-D [R, d] tensor")
+    Q = idx.shape[-1]
+    lead = tuple(idx.shape[:-1])
+    T = int(np.prod(lead)) if lead else 1
+    R, d = table_data.shape
+    dev = idx.device
+    row_offset = _host_array(row_offset, np.int64, (Q,), "row_offset")
+    rows = _host_array(rows, np.uint32, (Q,), "rows")
+    idx2 = idx.reshape(T, Q)
+    if out is None:
+        out = torch.empty((*lead, Q, d), dtype=torch.bfloat16, device=dev)
+    ip = _need(idx2, "idx", torch.int32, (T, Q), dev)
+    tp = _need(table_data, "table_data", torch.bfloat16, (R, d), dev)
+    op = _need(out.view(T, Q, d), "out", torch.bfloat16, (T, Q, d), dev)
+    st = load_library().tk_engram_gather(
+        ip, T, Q, tp, R, d, ctypes.c_void_p(row_offset.ctypes.data),
+        ctypes.c_void_p(rows.ctypes.data), op, _stream_handle(dev, stream))
+    _check("tk_engram_gather", st)
     return out
 

@@ -178,6 +178,36 @@ tk_status tk_engram_hash(const int32_t* tokens, int64_t B, int64_t S, int32_t L,
                          void* stream);
 
 /*
+ * Hashed multi-table gather (section "5. Engram": the N-gram hashed embedding
+ * tables with O(1) retrieval that tk_engram_hash indexes). The Q tables are
+ * packed in one bf16 buffer; table q holds rows [row_offset[q],
+ * row_offset[q] + rows[q]). For token t and table q:
+ *
+ *   out[t][q][:] = table_data[row_offset[q] + idx[t][q]][:]   if 0 <= idx[t][q] < rows[q]
+ *   out[t][q][:] = 0                                          otherwise
+ *
+ *   idx        : int32 [T, Q], device, 4-byte aligned (e.g. tk_engram_hash's
+ *                output with Q = L * K)
+ *   table_data : bf16 [total_rows, d], device, 16-byte aligned
+ *   row_offset : int64 [Q], HOST; rows : uint32 [Q], HOST; every table must
+ *                lie inside [0, total_rows)
+ *   out        : bf16 [T, Q, d], device, 16-byte aligned
+ *
+ * Limits: 1 <= Q <= TK_ENGRAM_GATHER_MAX_TABLES, d a multiple of 8 and at
+ * most TK_ENGRAM_GATHER_MAX_D, T < 2^31. T = 0 is a successful no-op. Every
+ * index is checked against its table on the device, so no index value reads
+ * outside the buffer. An exact copy: results are bit-identical to any
+ * correct gather.
+ */
+#define TK_ENGRAM_GATHER_MAX_TABLES 32
+#define TK_ENGRAM_GATHER_MAX_D 8192
+
+tk_status tk_engram_gather(const int32_t* idx, int64_t T, int32_t Q,
+                           const uint16_t* table_data, int64_t total_rows, int64_t d,
+                           const int64_t* row_offset, const uint32_t* rows,
+                           uint16_t* out, void* stream);
+
+/*
  * Measurement aid, not part of the gate: copies `bytes` bytes (a multiple
  * of 16, both pointers 16-byte aligned) with the same 128-bit access width
  * as the gate kernels, to calibrate hardware byte counters and to give the

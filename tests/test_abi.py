@@ -203,3 +203,32 @@ def test_hash_argument_checks():
     assert hsh(out=None) == B.TK_ERR_NULL
     assert hsh(tokens=A16 + 2) == B.TK_ERR_ALIGN
     assert hsh(out=A16 + 4) == B.TK_ERR_ALIGN
+
+
+def gat(**kw):
+    import numpy as np
+    a = dict(idx=A16, T=4, Q=2, data=A16, R=100, d=64, off=[0, 50], rows=[50, 50], out=A16)
+    a.update(kw)
+    off = np.ascontiguousarray(a["off"], dtype=np.int64)
+    rows = np.ascontiguousarray(a["rows"], dtype=np.uint32)
+    return eg.load_library().tk_engram_gather(
+        a["idx"], a["T"], a["Q"], a["data"], a["R"], a["d"], off.ctypes.data,
+        rows.ctypes.data, a["out"], None)
+
+
+def test_gather_argument_checks():
+    assert gat(T=-1) == B.TK_ERR_SHAPE
+    assert gat(Q=0) == B.TK_ERR_SHAPE
+    assert gat(d=0) == B.TK_ERR_SHAPE
+    assert gat(d=12) == B.TK_ERR_ALIGN
+    assert gat(Q=33, off=[0] * 33, rows=[1] * 33) == B.TK_ERR_UNSUPPORTED
+    assert gat(d=8200) == B.TK_ERR_UNSUPPORTED
+    assert gat(off=[0, 51]) == B.TK_ERR_VALUE           # table 1 runs past R
+    assert gat(off=[-1, 50]) == B.TK_ERR_VALUE
+    assert gat(rows=[50, 51]) == B.TK_ERR_VALUE
+    assert gat(T=0, idx=None, data=None, out=None) == B.TK_SUCCESS
+    for name in ("idx", "data", "out"):
+        assert gat(**{name: None}) == B.TK_ERR_NULL, name
+    assert gat(idx=A16 + 2) == B.TK_ERR_ALIGN
+    assert gat(data=A16 + 8) == B.TK_ERR_ALIGN
+    assert gat(out=A4) == B.TK_ERR_ALIGN
