@@ -24,6 +24,7 @@ from ._binding import (  # noqa: F401
     tk_engram_gate_bwd,
     tk_engram_gate_fwd,
     tk_engram_grad_w_reduce,
+    tk_engram_fused_weight,
     tk_engram_gather,
     tk_engram_hash,
     tk_engram_num_partials,

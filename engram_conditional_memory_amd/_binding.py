@@ -30,7 +30,7 @@ EXPORTS = (
     "tk_engram_gate_fwd", "tk_engram_gate_bwd", "tk_engram_grad_w_reduce",
     "tk_engram_num_partials", "tk_engram_bwd_workspace_bytes",
     "tk_engram_copy_probe", "tk_status_string", "tk_abi_version", "tk_engram_hash",
-    "tk_engram_gather",
+    "tk_engram_gather", "tk_engram_fused_weight",
 )
 
 HASH_MAX_NGRAM = 4
@@ -78,6 +78,8 @@ def load_library(path: str = LIB) -> ctypes.CDLL:
     L.tk_engram_hash.restype = i32
     L.tk_engram_gather.argtypes = [vp, i64, i32, vp, i64, i64, vp, vp, vp, vp]
     L.tk_engram_gather.restype = i32
+    L.tk_engram_fused_weight.argtypes = [vp, vp, vp, i64, vp]
+    L.tk_engram_fused_weight.restype = i32
     _lib = L
     return L
 
@@ -361,4 +363,20 @@ def tk_engram_gather(idx, table_data, row_offset, rows, out=None, stream=None):
         ctypes.c_void_p(rows.ctypes.data), op, _stream_handle(dev, stream))
     _check("tk_engram_gather", st)
     return out
+
+
+def tk_engram_fused_weight(wh, we, w=None, stream=None):
+    """w = wh * we in fp64 (exact), from fp32 [H] GPU tensors."""
+    torch = _torch()
+    if not isinstance(wh, torch.Tensor) or wh.dim() != 1 or wh.device.type != "cuda":
+        raise ValueError("wh must be a 1-D fp32 GPU tensor")
+    H = wh.shape[0]
+    dev = wh.device
+    if w is None:
+        w = torch.empty((H,), dtype=torch.float64, device=dev)
+    st = load_library().tk_engram_fused_weight(
+        _need(wh, "wh", torch.float32, (H,), dev), _need(we, "we", torch.float32, (H,), dev),
+        _need(w, "w", torch.float64, (H,), dev), H, _stream_handle(dev, stream))
+    _check("tk_engram_fused_weight", st)
+    return w
 

@@ -587,6 +587,16 @@ __global__ __launch_bounds__(kRedCols4* kRedSlices) void grad_w_reduce_kernel(
   }
 }
 
+// ---- fused weight ------------------------------------------------------------
+
+// w_i = wh_i * we_i in fp64: the product of two fp32 values is exact there.
+__global__ __launch_bounds__(256) void fused_weight_kernel(const float* __restrict__ wh,
+                                                           const float* __restrict__ we,
+                                                           double* __restrict__ w, int64_t H) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < H) w[i] = (double)wh[i] * (double)we[i];
+}
+
 // ---- copy probe ------------------------------------------------------------
 
 // Each block copies contiguous 16 KiB tiles (256 threads x 4 chunks), tiles
@@ -867,6 +877,19 @@ tk_status tk_engram_grad_w_reduce(const float* workspace, int64_t P, int64_t H,
   void* args[] = {&ws, &P, &nq, &a, &b, &oh, &oe};
   const int grid = (nq + kRedCols4 - 1) / kRedCols4;
   return launch(grad_w_reduce_kernel, grid, kRedCols4 * kRedSlices, args,
+                reinterpret_cast<hipStream_t>(stream));
+}
+
+tk_status tk_engram_fused_weight(const float* wh, const float* we, double* w, int64_t H,
+                                 void* stream) {
+  if (H < 0) return TK_ERR_SHAPE;
+  if (H == 0) return TK_SUCCESS;
+  if (!wh || !we || !w) return TK_ERR_NULL;
+  if (((uintptr_t)wh & 3u) || ((uintptr_t)we & 3u) || ((uintptr_t)w & 7u)) return TK_ERR_ALIGN;
+  if (H > ((int64_t)1 << 40)) return TK_ERR_UNSUPPORTED;
+  const int64_t blocks = (H + 255) / 256;
+  void* args[] = {&wh, &we, &w, &H};
+  return launch(fused_weight_kernel, (int)blocks, 256, args,
                 reinterpret_cast<hipStream_t>(stream));
 }
 

@@ -142,6 +142,24 @@ tk_status tk_engram_grad_w_reduce(const float* workspace, int64_t P, int64_t H,
                                   float* dwe, void* stream);
 
 /*
+ * Fused RMSNorm weight (section "5. Engram": engram_fused_weight, the weight
+ * preprocessing step). The two RMSNorm weights enter the gate only through
+ * their product, since dot(RMSNorm(x, wh), RMSNorm(k, we)) =
+ * r_x * r_k * sum_i x_i k_i (wh_i * we_i); this call forms that product,
+ *
+ *   w[i] = wh[i] * we[i]    in fp64, exactly (a product of two fp32 values)
+ *
+ *   wh, we : fp32 [H], device, 4-byte aligned
+ *   w      : fp64 [H], device, 8-byte aligned
+ *
+ * The gate calls above form the same exact products themselves (they are
+ * O(H) per launch), so they take wh and we; this call is for callers that
+ * keep the fused weight. H = 0 is a successful no-op.
+ */
+tk_status tk_engram_fused_weight(const float* wh, const float* we, double* w, int64_t H,
+                                 void* stream);
+
+/*
  * N-gram hash of the Engram memory (section "5. Engram": engram_hash, the
  * step before the gate: N-gram token ids combined by XOR and multiplication
  * and mapped to embedding-table indices; the page describes 2 N-gram layers,

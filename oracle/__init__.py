@@ -250,3 +250,12 @@ def engram_gather(idx, table_data, row_offset, rows):
     out[~valid] = 0
     return out
 
+
+# ---- fused RMSNorm weight ---------------------------------------------------------
+
+def fused_weight(wh, we):
+    """w = wh * we for fp32 inputs, in fp64 (the product of two 24-bit
+    significands has at most 48 bits, so it is exact in fp64)."""
+    return np.asarray(wh, dtype=np.float32).astype(np.float64) * \
+        np.asarray(we, dtype=np.float32).astype(np.float64)
+

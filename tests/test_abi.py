@@ -232,3 +232,12 @@ def test_gather_argument_checks():
     assert gat(idx=A16 + 2) == B.TK_ERR_ALIGN
     assert gat(data=A16 + 8) == B.TK_ERR_ALIGN
     assert gat(out=A4) == B.TK_ERR_ALIGN
+
+
+def test_fused_weight_argument_checks():
+    L = eg.load_library()
+    assert L.tk_engram_fused_weight(A16, A16, A16, -1, None) == B.TK_ERR_SHAPE
+    assert L.tk_engram_fused_weight(None, None, None, 0, None) == B.TK_SUCCESS
+    assert L.tk_engram_fused_weight(None, A16, A16, 8, None) == B.TK_ERR_NULL
+    assert L.tk_engram_fused_weight(A16, A16, A4, 8, None) == B.TK_ERR_ALIGN
+    assert L.tk_engram_fused_weight(A16 + 2, A16, A16, 8, None) == B.TK_ERR_ALIGN

@@ -292,3 +292,17 @@ def test_copy_probe(eg, cuda_device):
     eg.tk_engram_copy_probe(src, dst)
     torch.cuda.synchronize()
     assert torch.equal(src, dst)
+
+
+# --------------------------------------------------------------- fused weight
+
+@pytest.mark.parametrize("H", [1, 7, 256, 7168, 100003])
+def test_fused_weight_is_the_exact_product(eg, cuda_device, H):
+    import torch
+    r = np.random.default_rng(H)
+    wh = (1 + 0.1 * r.standard_normal(H)).astype(np.float32)
+    we = (r.standard_normal(H) * 10.0 ** r.integers(-30, 30, H)).astype(np.float32)
+    w = eg.tk_engram_fused_weight(torch.from_numpy(wh).to(cuda_device),
+                                  torch.from_numpy(we).to(cuda_device))
+    torch.cuda.synchronize()
+    assert np.array_equal(w.cpu().numpy(), oracle.fused_weight(wh, we))

@@ -355,3 +355,15 @@ def test_oracle_snapshot_config1():
         assert np.allclose(got, want, rtol=1e-12, atol=1e-14)
     for i, want in cols.items():
         assert np.allclose([dwh[i], dwe[i]], want, rtol=1e-12, atol=1e-14)
+
+
+def test_fused_weight_is_exact():
+    # the fused weight of the "5. Engram" section's weight preprocessing:
+    # wh * we formed in fp64 equals the exact rational product
+    from fractions import Fraction
+    r = np.random.default_rng(41)
+    wh = (r.standard_normal(500) * 10.0 ** r.integers(-20, 20, 500)).astype(np.float32)
+    we = (r.standard_normal(500) * 10.0 ** r.integers(-20, 20, 500)).astype(np.float32)
+    w = oracle.fused_weight(wh, we)
+    for a, b, c in zip(wh, we, w):
+        assert Fraction(float(a)) * Fraction(float(b)) == Fraction(float(c))
