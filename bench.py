@@ -231,6 +231,22 @@ def copy_ceiling(nbytes: int, eg, dev, reps: int = 20) -> dict:
             "frac": 2 * nbytes / (us * 1e3) / HBM_PEAK_GBPS}
 
 
+def mix_ceiling(nsrc: int, ndst: int, nbytes: int, eg, dev, reps: int = 20) -> dict:
+    """Practical HBM ceiling of a read/write mix: the library's stream probe
+    with nsrc input and ndst output streams of nbytes each, random data."""
+    import torch
+    n = nbytes // 4
+    srcs = [torch.randint(-(1 << 31), (1 << 31) - 1, (n,), dtype=torch.int32, device=dev)
+            for _ in range(nsrc)]
+    dsts = [torch.empty_like(srcs[0]) for _ in range(ndst)]
+    us = avg_launch_us(lambda: eg.tk_engram_stream_probe(srcs, dsts), reps)
+    moved = (nsrc + ndst) * nbytes
+    del srcs, dsts
+    torch.cuda.empty_cache()
+    return {"reads": nsrc, "writes": ndst, "bytes_each": nbytes, "us": us,
+            "GBps": moved / (us * 1e3), "frac": moved / (us * 1e3) / HBM_PEAK_GBPS}
+
+
 def cpu_baseline(host: dict, budget_s: float = 10.0) -> dict:
     """The fp64 oracle, as it stands, on the host cores: forward + backward
     (incl. dwh/dwe) over the workload's tokens in chunks, repeating passes
@@ -366,6 +382,13 @@ def main():
         torch.cuda.empty_cache()
 
     copy = copy_ceiling(2 * main_res["T"] * main_res["H"], eg, dev)
+    print("[bench] measuring the read/write-mix ceilings", file=sys.stderr, flush=True)
+    tensor_bytes = 2 * main_res["T"] * main_res["H"]
+    ceilings = {"fwd_3r1w": mix_ceiling(3, 1, tensor_bytes, eg, dev),
+                "bwd_4r3w": mix_ceiling(4, 3, tensor_bytes, eg, dev)}
+    main_res["fwd"]["frac_of_mix_ceiling"] = main_res["fwd"]["GBps"] / ceilings["fwd_3r1w"]["GBps"]
+    main_res["bwd_kernel"]["frac_of_mix_ceiling"] = (main_res["bwd_kernel"]["GBps"]
+                                                     / ceilings["bwd_4r3w"]["GBps"])
     print("[bench] timing the N-gram hash", file=sys.stderr, flush=True)
     hash_res = time_hash(eg, dev)
     print("[bench] timing the hashed gather", file=sys.stderr, flush=True)
@@ -403,6 +426,7 @@ def main():
         "reduce_us": main_res["reduce_us"],
         "secondary": secondary,
         "copy_probe": copy,
+        "mix_ceilings": ceilings,
         "hash": hash_res,
         "gather": gather_res,
         "cpu_baseline": cpu,

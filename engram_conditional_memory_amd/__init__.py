@@ -28,6 +28,7 @@ from ._binding import (  # noqa: F401
     tk_engram_gather,
     tk_engram_hash,
     tk_engram_num_partials,
+    tk_engram_stream_probe,
     tk_status_string,
 )
 from .build import LIB as LIBRARY_PATH  # noqa: F401

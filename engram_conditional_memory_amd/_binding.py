@@ -30,7 +30,7 @@ EXPORTS = (
     "tk_engram_gate_fwd", "tk_engram_gate_bwd", "tk_engram_grad_w_reduce",
     "tk_engram_num_partials", "tk_engram_bwd_workspace_bytes",
     "tk_engram_copy_probe", "tk_status_string", "tk_abi_version", "tk_engram_hash",
-    "tk_engram_gather", "tk_engram_fused_weight",
+    "tk_engram_gather", "tk_engram_fused_weight", "tk_engram_stream_probe",
 )
 
 HASH_MAX_NGRAM = 4
@@ -80,6 +80,8 @@ def load_library(path: str = LIB) -> ctypes.CDLL:
     L.tk_engram_gather.restype = i32
     L.tk_engram_fused_weight.argtypes = [vp, vp, vp, i64, vp]
     L.tk_engram_fused_weight.restype = i32
+    L.tk_engram_stream_probe.argtypes = [vp, i32, vp, i32, sz, vp]
+    L.tk_engram_stream_probe.restype = i32
     _lib = L
     return L
 
@@ -379,4 +381,21 @@ def tk_engram_fused_weight(wh, we, w=None, stream=None):
         _need(w, "w", torch.float64, (H,), dev), H, _stream_handle(dev, stream))
     _check("tk_engram_fused_weight", st)
     return w
+
+
+def tk_engram_stream_probe(srcs, dsts, stream=None):
+    """Stream every tensor of `srcs` in and write every tensor of `dsts` (all
+    GPU tensors of one byte size) with the library's tiled probe kernel."""
+    if not srcs or not dsts:
+        raise ValueError("need at least one source and one destination")
+    n = srcs[0].numel() * srcs[0].element_size()
+    for t in list(srcs) + list(dsts):
+        if t.numel() * t.element_size() != n or not t.is_contiguous():
+            raise ValueError("all probe tensors must be contiguous and of one byte size")
+    src = (ctypes.c_void_p * len(srcs))(*[t.data_ptr() for t in srcs])
+    dst = (ctypes.c_void_p * len(dsts))(*[t.data_ptr() for t in dsts])
+    st = load_library().tk_engram_stream_probe(
+        ctypes.cast(src, ctypes.c_void_p), len(srcs), ctypes.cast(dst, ctypes.c_void_p),
+        len(dsts), n, _stream_handle(srcs[0].device, stream))
+    _check("tk_engram_stream_probe", st)
 

@@ -622,6 +622,52 @@ __global__ __launch_bounds__(256) void copy_probe_kernel(
     dst[i] = src[i];
 }
 
+// ---- stream-mix probe -------------------------------------------------------
+
+// R input streams and S output streams of n 16-byte chunks each, in the same
+// tiled nontemporal pattern as the copy probe: output o is the XOR of all
+// inputs plus o, so no load is dead. Measures the practical HBM ceiling of a
+// kernel's read/write mix (the forward reads 3 and writes 1 stream, the
+// backward reads 4 and writes 3).
+struct StreamSet {
+  const u32x4* in[TK_ENGRAM_PROBE_MAX_STREAMS];
+  u32x4* out[TK_ENGRAM_PROBE_MAX_STREAMS];
+};
+
+template <int R, int S>
+__global__ __launch_bounds__(256) void stream_probe_kernel(StreamSet st, int64_t n) {
+  constexpr int64_t tile = 256 * kCopyUnroll;
+  const int64_t ntile = n / tile;
+  for (int64_t t = blockIdx.x; t < ntile; t += gridDim.x) {
+    const int64_t base = t * tile + threadIdx.x;
+    u32x4 a[R][kCopyUnroll];
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+#pragma unroll
+      for (int u = 0; u < kCopyUnroll; ++u)
+        a[i][u] = __builtin_nontemporal_load(st.in[i] + base + u * 256);
+#pragma unroll
+    for (int o = 0; o < S; ++o)
+#pragma unroll
+      for (int u = 0; u < kCopyUnroll; ++u) {
+        u32x4 x = a[0][u];
+#pragma unroll
+        for (int i = 1; i < R; ++i) x ^= a[i][u] + (uint32_t)o;
+        store_chunk(st.out[o] + base + u * 256, x);
+      }
+  }
+  for (int64_t i = ntile * tile + (int64_t)blockIdx.x * 256 + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * 256) {
+#pragma unroll
+    for (int o = 0; o < S; ++o) {
+      u32x4 x = st.in[0][i];
+#pragma unroll
+      for (int k = 1; k < R; ++k) x ^= st.in[k][i] + (uint32_t)o;
+      st.out[o][i] = x;
+    }
+  }
+}
+
 // ---- host side -------------------------------------------------------------
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -906,6 +952,40 @@ tk_status tk_engram_copy_probe(const void* src, void* dst, size_t bytes,
   void* args[] = {&s, &d, &n};
   return launch(copy_probe_kernel, grid, 256, args,
                 reinterpret_cast<hipStream_t>(stream));
+}
+
+tk_status tk_engram_stream_probe(const void* const* src, int32_t nsrc, void* const* dst,
+                                 int32_t ndst, size_t bytes, void* stream) {
+  if (nsrc < 1 || ndst < 1 || nsrc > TK_ENGRAM_PROBE_MAX_STREAMS ||
+      ndst > TK_ENGRAM_PROBE_MAX_STREAMS)
+    return TK_ERR_SHAPE;
+  if (!src || !dst) return TK_ERR_NULL;
+  if (bytes == 0) return TK_SUCCESS;
+  if (bytes & 15u) return TK_ERR_ALIGN;
+  StreamSet st = {};
+  for (int i = 0; i < nsrc; ++i) {
+    if (!src[i]) return TK_ERR_NULL;
+    if (!aligned16(src[i])) return TK_ERR_ALIGN;
+    st.in[i] = reinterpret_cast<const u32x4*>(src[i]);
+  }
+  for (int o = 0; o < ndst; ++o) {
+    if (!dst[o]) return TK_ERR_NULL;
+    if (!aligned16(dst[o])) return TK_ERR_ALIGN;
+    st.out[o] = reinterpret_cast<u32x4*>(dst[o]);
+  }
+  int64_t n = (int64_t)(bytes / 16);
+  const int64_t tiles = (n + 256 * kCopyUnroll - 1) / (256 * kCopyUnroll);
+  const int grid = (int)(tiles < 32768 ? tiles : 32768);
+  void* args[] = {&st, &n};
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+#define TK_PROBE(R, S) \
+  if (nsrc == R && ndst == S) return launch(stream_probe_kernel<R, S>, grid, 256, args, hs)
+  TK_PROBE(1, 1); TK_PROBE(2, 1); TK_PROBE(3, 1); TK_PROBE(4, 1);
+  TK_PROBE(1, 2); TK_PROBE(2, 2); TK_PROBE(3, 2); TK_PROBE(4, 2);
+  TK_PROBE(1, 3); TK_PROBE(2, 3); TK_PROBE(3, 3); TK_PROBE(4, 3);
+  TK_PROBE(1, 4); TK_PROBE(2, 4); TK_PROBE(3, 4); TK_PROBE(4, 4);
+#undef TK_PROBE
+  return TK_ERR_UNSUPPORTED;
 }
 
 }  // extern "C"

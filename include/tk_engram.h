@@ -234,6 +234,20 @@ tk_status tk_engram_gather(const int32_t* idx, int64_t T, int32_t Q,
 tk_status tk_engram_copy_probe(const void* src, void* dst, size_t bytes,
                                void* stream);
 
+/*
+ * Measurement aid, not part of the gate: streams nsrc input buffers and
+ * writes ndst output buffers of `bytes` bytes each (a multiple of 16, every
+ * pointer 16-byte aligned; src and dst are HOST arrays of device pointers),
+ * output o being the XOR of all inputs plus o, in the same tiled
+ * nontemporal pattern as tk_engram_copy_probe. It gives the practical HBM
+ * ceiling of a kernel's read/write mix: 3 in / 1 out for the forward, 4 in /
+ * 3 out for the backward. 1 <= nsrc, ndst <= TK_ENGRAM_PROBE_MAX_STREAMS.
+ */
+#define TK_ENGRAM_PROBE_MAX_STREAMS 4
+
+tk_status tk_engram_stream_probe(const void* const* src, int32_t nsrc, void* const* dst,
+                                 int32_t ndst, size_t bytes, void* stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* tk_status_string(tk_status s);
 

@@ -241,3 +241,19 @@ def test_fused_weight_argument_checks():
     assert L.tk_engram_fused_weight(None, A16, A16, 8, None) == B.TK_ERR_NULL
     assert L.tk_engram_fused_weight(A16, A16, A4, 8, None) == B.TK_ERR_ALIGN
     assert L.tk_engram_fused_weight(A16 + 2, A16, A16, 8, None) == B.TK_ERR_ALIGN
+
+
+def test_stream_probe_argument_checks():
+    import ctypes
+    L = eg.load_library()
+    two = (ctypes.c_void_p * 2)(A16, A16)
+    bad = (ctypes.c_void_p * 2)(A16, A4)
+    nul = (ctypes.c_void_p * 2)(A16, None)
+    c = lambda a: ctypes.cast(a, ctypes.c_void_p)
+    assert L.tk_engram_stream_probe(c(two), 0, c(two), 1, 64, None) == B.TK_ERR_SHAPE
+    assert L.tk_engram_stream_probe(c(two), 1, c(two), 5, 64, None) == B.TK_ERR_SHAPE
+    assert L.tk_engram_stream_probe(None, 1, c(two), 1, 64, None) == B.TK_ERR_NULL
+    assert L.tk_engram_stream_probe(c(two), 2, c(two), 2, 0, None) == B.TK_SUCCESS
+    assert L.tk_engram_stream_probe(c(two), 2, c(two), 2, 40, None) == B.TK_ERR_ALIGN
+    assert L.tk_engram_stream_probe(c(bad), 2, c(two), 1, 64, None) == B.TK_ERR_ALIGN
+    assert L.tk_engram_stream_probe(c(two), 1, c(nul), 2, 64, None) == B.TK_ERR_NULL

@@ -285,6 +285,19 @@ def test_side_stream_and_identity(eg, cuda_device):
     assert np.max(np.abs(lhs - rhs)) <= 1e-6 * np.max(np.abs(lhs))
 
 
+def test_stream_probe(eg, cuda_device):
+    import torch
+    n = (1 << 20) + 12                  # not a whole tile: exercises the tail
+    srcs = [torch.randint(-(1 << 31), (1 << 31) - 1, (n,), dtype=torch.int32,
+                          device=cuda_device) for _ in range(3)]
+    dsts = [torch.zeros_like(srcs[0]) for _ in range(2)]
+    eg.tk_engram_stream_probe(srcs, dsts)
+    torch.cuda.synchronize()
+    x = srcs[0] ^ srcs[1] ^ srcs[2]
+    assert torch.equal(dsts[0], x)
+    assert torch.equal(dsts[1], srcs[0] ^ (srcs[1] + 1) ^ (srcs[2] + 1))
+
+
 def test_copy_probe(eg, cuda_device):
     import torch
     src = torch.arange(1 << 20, dtype=torch.int32, device=cuda_device)
