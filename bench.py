@@ -247,6 +247,43 @@ def mix_ceiling(nsrc: int, ndst: int, nbytes: int, eg, dev, reps: int = 20) -> d
             "GBps": moved / (us * 1e3), "frac": moved / (us * 1e3) / HBM_PEAK_GBPS}
 
 
+def time_fwd_small(eg, dev, reps: int = 50) -> dict:
+    """The forward-only workload (batch 2 x seq 512 = 1024 tokens, H=4096,
+    33.6 MB): it fits the 256 MB Infinity Cache, so it is timed two ways:
+    hot (back-to-back launches) and flushed (a 1 GiB write between launches,
+    each launch timed alone with its own events)."""
+    import synth
+    import torch
+    c = synth.CONFIGS[2]
+    d = synth.make_inputs(2, with_grad=False)
+    x, k, v = to_dev(d["x"], dev), to_dev(d["k"], dev), to_dev(d["v"], dev)
+    wh = torch.from_numpy(d["wh"]).to(dev)
+    we = torch.from_numpy(d["we"]).to(dev)
+    out = torch.empty_like(x)
+    gate = torch.empty((c.T,), dtype=torch.float32, device=dev)
+    fwd = eg.bind_gate_fwd(x, k, v, wh, we, out, gate)
+    hot = avg_launch_us(fwd, reps)
+    scrub = torch.empty(1 << 29, dtype=torch.int16, device=dev)
+    times = []
+    for i in range(reps):
+        scrub.fill_(i)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        fwd()
+        b.record()
+        torch.cuda.synchronize()
+        times.append(1e3 * a.elapsed_time(b))
+    flushed = float(np.median(times))
+    nbytes = algorithmic_bytes(c.T, c.H)["fwd"]
+    del x, k, v, out, gate, scrub, fwd
+    torch.cuda.empty_cache()
+    return {"workload": c.name, "T": c.T, "H": c.H, "bytes": nbytes,
+            "hot_us": hot, "hot_GBps": nbytes / (hot * 1e3),
+            "flushed_us": flushed, "flushed_GBps": nbytes / (flushed * 1e3),
+            "flushed_frac": nbytes / (flushed * 1e3) / HBM_PEAK_GBPS}
+
+
 def cpu_baseline(host: dict, budget_s: float = 10.0) -> dict:
     """The fp64 oracle, as it stands, on the host cores: forward + backward
     (incl. dwh/dwe) over the workload's tokens in chunks, repeating passes
@@ -345,7 +382,8 @@ def main():
                     help="main workload (3: T=16384 H=4096, 4: T=32768 H=7168, 5: stress)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true",
-                    help="skip the second tuned width")
+                    help="skip the other workloads (second width, stress, small forward, "
+                         "memory read)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="summarise two rocprofv3 --pmc runs instead of benchmarking")
     args = ap.parse_args()
@@ -381,6 +419,18 @@ def main():
         del w2
         torch.cuda.empty_cache()
 
+    stress = small = None
+    if not args.no_secondary:
+        if args.workload != 5:
+            print("[bench] generating workload 5 (stress, T=65537)", file=sys.stderr, flush=True)
+            w5 = Workload(5, dev, eg)
+            stress = time_workload(w5, min(args.steps, 20), args.warmup)
+            w5.free()
+            del w5
+            torch.cuda.empty_cache()
+        print("[bench] timing the small forward", file=sys.stderr, flush=True)
+        small = time_fwd_small(eg, dev)
+
     copy = copy_ceiling(2 * main_res["T"] * main_res["H"], eg, dev)
     print("[bench] measuring the read/write-mix ceilings", file=sys.stderr, flush=True)
     tensor_bytes = 2 * main_res["T"] * main_res["H"]
@@ -389,10 +439,12 @@ def main():
     main_res["fwd"]["frac_of_mix_ceiling"] = main_res["fwd"]["GBps"] / ceilings["fwd_3r1w"]["GBps"]
     main_res["bwd_kernel"]["frac_of_mix_ceiling"] = (main_res["bwd_kernel"]["GBps"]
                                                      / ceilings["bwd_4r3w"]["GBps"])
-    print("[bench] timing the N-gram hash", file=sys.stderr, flush=True)
-    hash_res = time_hash(eg, dev)
-    print("[bench] timing the hashed gather", file=sys.stderr, flush=True)
-    gather_res = time_gather(eg, dev)
+    hash_res = gather_res = None
+    if not args.no_secondary:
+        print("[bench] timing the N-gram hash", file=sys.stderr, flush=True)
+        hash_res = time_hash(eg, dev)
+        print("[bench] timing the hashed gather", file=sys.stderr, flush=True)
+        gather_res = time_gather(eg, dev)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -425,6 +477,8 @@ def main():
         "bwd_kernel": bk,
         "reduce_us": main_res["reduce_us"],
         "secondary": secondary,
+        "stress": stress,
+        "fwd_small": small,
         "copy_probe": copy,
         "mix_ceilings": ceilings,
         "hash": hash_res,
