@@ -392,8 +392,10 @@ def main():
         print(json.dumps(rec, indent=1, sort_keys=True))
         return
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not "
-              "supported (the path shards by tokens; see the design notes).", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported. The gate "
+              "shards by tokens: each GPU runs these kernels on its share of the rows, and "
+              "the only exchange is one all-reduce of the H-wide weight-gradient vector.",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -8,7 +8,7 @@
 // with XOR and multiplication into a hash value and maps it to an index of
 // an embedding table; there are 2 N-gram layers, N up to 3, and 8 tables per
 // layer. The page fixes nothing else, so the rest is a reading, stated here
-// and in the design notes:
+// (the plainest one: the caller's constants, the usual modulus map):
 //
 //   * token ids are int32, taken as their 32-bit unsigned pattern;
 //   * layer l uses the last n_l tokens of the sequence up to and including

@@ -14,13 +14,17 @@
 // weight-gradient reduction; the juejin.cn page (highlight 5) says the
 // autograd wrapper covers forward, backward and weight-gradient reduction.
 //
-// Readings where the page is silent (each is listed with its reason in the
-// design notes of the repository):
-//   * hidden_states is the same row x that is normalised;
-//   * RMSNorm(x, w)_i = x_i / sqrt(mean(x^2) + eps) * w_i, eps inside the root;
-//   * sign(0) = 0, so a zero dot gives gate = 1/2;
+// Readings where the page is silent, each with its reason:
+//   * hidden_states is the same row x that is normalised (the formula uses
+//     both names for the one residual row);
+//   * RMSNorm(x, w)_i = x_i / sqrt(mean(x^2) + eps) * w_i, eps inside the
+//     root, eps = 1e-6 (the usual RMSNorm; the page gives no eps);
+//   * sign(0) = 0, so a zero dot gives gate = 1/2 (the sign function's
+//     usual value at 0);
 //   * the derivative of signed_sqrt, 1 / (2 sqrt|z|), is evaluated as
-//     1 / (2 sqrt(max(|z|, clamp))) so that it stays finite at z = 0;
+//     1 / (2 sqrt(max(|z|, clamp))) so that it stays finite at z = 0, where
+//     the true derivative is infinite (the clamp is a convention shared with
+//     the GPU library, not a consequence of the formula);
 //   * the backward is the chain rule of the forward, nothing else.
 //
 // Everything is fp64, row by row, with every intermediate of the formula

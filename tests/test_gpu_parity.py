@@ -1,10 +1,15 @@
 """GPU parity: the HIP library (through its C ABI) against the fp64 oracle.
 
-Tolerances (written here, derived in the design notes):
+Tolerances, and where they come from:
   gate            max |gpu - oracle| <= 1e-5
   out             within 1 bf16 ulp of bf16(oracle), or, where x and gate*v
-                  cancel, |gpu - oracle| <= 1e-5 |v| + 2^-24 (|x| + |gate v|)
-  dx, dk, dv      relative L2 error <= 1e-3 against bf16(oracle)
+                  cancel, |gpu - oracle| <= 1e-5 |v| + 2^-24 (|x| + |gate v|):
+                  a gate within 1e-5 and one fp32 rounding of x + gate*v
+                  allow exactly that much where the result is tiny
+  dx, dk, dv      relative L2 error <= 1e-3 against bf16(oracle): the
+                  outputs are bf16, whose rounding alone is ~1.7e-3 relative
+                  L2 against unrounded fp64, so they are compared with the
+                  oracle's value rounded once to bf16
   dwh, dwe        relative L2 error <= 1e-3 against the oracle (fp32 outputs)
   reruns          bit-identical
 Full-size workloads are compared on every element, streaming the oracle over
