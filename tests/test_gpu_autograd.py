@@ -7,6 +7,7 @@ import numpy as np
 import pytest
 
 import oracle
+import synth
 
 pytestmark = pytest.mark.gpu
 
@@ -22,8 +23,8 @@ def eg(cuda_device):
 
 def case(T, H, seed):
     r = np.random.default_rng(seed)
-    d = {n: oracle.round_bf16(r.standard_normal((T, H))) for n in ("x", "k", "v", "grad_out")}
-    d["k"] = oracle.round_bf16(oracle.bf16_to_f64(d["k"]) + 0.5 * oracle.bf16_to_f64(d["x"]))
+    d = {n: synth.round_bf16(r.standard_normal((T, H))) for n in ("x", "k", "v", "grad_out")}
+    d["k"] = synth.round_bf16(synth.bf16_to_f64(d["k"]) + 0.5 * synth.bf16_to_f64(d["x"]))
     d["wh"] = (1 + 0.1 * r.standard_normal(H)).astype(np.float32)
     d["we"] = (1 + 0.1 * r.standard_normal(H)).astype(np.float32)
     return d

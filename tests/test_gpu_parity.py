@@ -206,7 +206,7 @@ def make_case(T, H, seed=0, fill=None):
     r = np.random.default_rng(seed)
     d = {"T": T, "H": H, "r0": 0, "config": synth.CONFIGS[1]}
     for n in ("x", "k", "v", "grad_out"):
-        d[n] = oracle.round_bf16(r.standard_normal((T, H)))
+        d[n] = synth.round_bf16(r.standard_normal((T, H)))
     d["wh"] = (1 + 0.1 * r.standard_normal(H)).astype(np.float32)
     d["we"] = (1 + 0.1 * r.standard_normal(H)).astype(np.float32)
     if fill:
@@ -238,7 +238,7 @@ def test_special_rows(eg, cuda_device):
         d["k"][5] = d["x"][4] ^ 0x8000
         d["x"][6, 1::2] = 0                      # orthogonal supports: gate 1/2
         d["k"][6, 0::2] = 0
-        big = oracle.round_bf16(oracle.bf16_to_f64(d["x"][7]) * 1e3)
+        big = synth.round_bf16(synth.bf16_to_f64(d["x"][7]) * 1e3)
         d["x"][7] = big                          # scaled row
     d = make_case(T, H, seed=5, fill=fill)
     g = run_gpu(eg, d, cuda_device)
