@@ -1,0 +1,62 @@
+"""bench.py without a GPU: the multi-GPU refusal, and the rocprofv3 counter
+summary that turns FETCH_SIZE / WRITE_SIZE into bytes per launch."""
+
+import csv
+import json
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and "shards by tokens" in r.stderr
+
+
+def _counter_csv(path, counter, rows):
+    fields = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=fields)
+        w.writeheader()
+        for i, (name, value) in enumerate(rows):
+            w.writerow({"Dispatch_Id": i, "Kernel_Name": name, "Counter_Name": counter,
+                        "Counter_Value": value})
+
+
+def test_traffic_summary_calibrates_on_the_copy_probe(tmp_path, monkeypatch):
+    import synth
+    c = synth.CONFIGS[4]
+    copy_bytes = 2 * c.T * c.H
+    fwd = "void (anonymous namespace)::gate_fwd_kernel<7, 2, true, 2>(unsigned int, int)"
+    bwd = "void (anonymous namespace)::gate_bwd_kernel<7, 2, true, 3, true>(int)"
+    cp = "(anonymous namespace)::copy_probe_kernel(unsigned int __vector(4) const*, long)"
+    # FETCH_SIZE reads half the bytes and WRITE_SIZE all of them, in KiB
+    _counter_csv(tmp_path / "f.csv", "FETCH_SIZE",
+                 [(cp, copy_bytes / 2048), (fwd, 3 * copy_bytes / 2 / 2048),
+                  (fwd, 3 * copy_bytes / 2 / 2048), (bwd, 2 * copy_bytes / 2048)])
+    _counter_csv(tmp_path / "w.csv", "WRITE_SIZE",
+                 [(cp, copy_bytes / 1024), (fwd, copy_bytes / 2 / 1024),
+                  (bwd, 3 * copy_bytes / 2 / 1024)])
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    rec = bench.traffic_from_counters(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), 4)
+    assert abs(rec["calibration"]["fetch_scale"] - 2.0) < 1e-12
+    assert abs(rec["calibration"]["write_scale"] - 1.0) < 1e-12
+    k = rec["kernels"]
+    # forward: 3 tensors read, 1 written; backward: 4 read, 3 written
+    assert abs(k["gate_fwd_kernel"]["bytes_per_launch"] - 2 * copy_bytes) < 1
+    assert abs(k["gate_bwd_kernel"]["bytes_per_launch"] - 3.5 * copy_bytes) < 1
+    saved = json.load(open(tmp_path / f"traffic_{c.name}.json"))
+    assert saved["kernel_source_sha256_16"] == bench.kernel_source_hash()
+    # the bench line uses it only while the kernel source is unchanged
+    assert bench.measured_traffic("gate_bwd_kernel", c.name) == \
+        k["gate_bwd_kernel"]["bytes_per_launch"]
+    saved["kernel_source_sha256_16"] = "0" * 16
+    json.dump(saved, open(tmp_path / f"traffic_{c.name}.json", "w"))
+    assert bench.measured_traffic("gate_bwd_kernel", c.name) is None
