@@ -371,3 +371,31 @@ def test_graph_capture_and_replay(eg, cuda_device):
         torch.cuda.synchronize()
         for a, b in zip((out, gate, dx, dk, dv, dwh, dwe), ref):
             assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), i
+
+
+# ------------------------------------------------ untuned widths at volume
+
+@pytest.mark.parametrize("T,H", [(20001, 3072), (8192, 8192)])
+def test_untuned_widths_many_rows_per_block(eg, cuda_device, T, H):
+    # the generic plans (masked tail chunks at H=3072; 8 waves x 2 chunks at
+    # H=8192) with ~30-80 rows per workgroup, compared on every element
+    d = make_case(T, H, seed=T + H)
+    g = run_gpu(eg, d, cuda_device)
+    assert_report(compare(d, g), name=f"T={T} H={H}")
+    assert_dv_is_gate_times_grad(d, g)
+
+
+def test_nan_row_stays_in_its_row(eg, cuda_device):
+    # rows are independent in the forward: a NaN in one token's hidden row
+    # gives that token a NaN gate and output and leaves every other row as
+    # the oracle computes it
+    T, H = 300, 4096
+    d = make_case(T, H, seed=99)
+    d["x"][17, 5] = 0x7FC0                       # bf16 quiet NaN
+    g = run_gpu(eg, d, cuda_device, backward=False)
+    assert np.isnan(g["gate"][17])
+    keep = np.ones(T, dtype=bool)
+    keep[17] = False
+    sub = {n: d[n][keep] for n in ("x", "k", "v")}
+    _, o_gate, _ = oracle.fwd_bf16(sub["x"], sub["k"], sub["v"], d["wh"], d["we"])
+    assert np.max(np.abs(g["gate"][keep] - o_gate)) <= GATE_TOL
