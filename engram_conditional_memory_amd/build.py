@@ -35,5 +35,23 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+EXAMPLE_SRC = os.path.join(ROOT, "tests", "c_abi", "gate_c_example.cpp")
+EXAMPLE = os.path.join(ROOT, "tests", "c_abi", "gate_c_example")
+
+
+def build_example(verbose: bool = False) -> str:
+    """Build the host-only C++ program that calls the library through its C ABI
+    (linked against the in-tree libtk_engram.so by relative rpath)."""
+    cmd = ["hipcc", "-O2", "-std=c++17", "-I", INCLUDE, EXAMPLE_SRC, "-L", PKG, "-ltk_engram",
+           "-Wl,-rpath,$ORIGIN/../../engram_conditional_memory_amd", "-o", EXAMPLE]
+    if verbose:
+        print(" ".join(cmd))
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed:\n{r.stdout}\n{r.stderr}")
+    return EXAMPLE
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_example(verbose=True))
