@@ -1,7 +1,8 @@
 """Engram gate for AMD MI355X: Python binding of the HIP library libtk_engram.so.
 
 The gate (zhichai.net TileKernels page, section "5. Engram", gate formula):
-    gate = sigmoid(signed_sqrt(dot(RMSNorm(x, wh), RMSNorm(k, we)) / sqrt(H)))
+    d    = <RMSNorm of x with weight wh, RMSNorm of k with weight we>
+    gate = sigmoid(sign(d) * sqrt(|d| / sqrt(H)))
     out  = x + gate * v
 with its backward (dx, dk, dv) and the weight-gradient reduction (dwh, dwe).
 The C ABI is declared in include/tk_engram.h; the functions below have the

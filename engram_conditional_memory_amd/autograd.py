@@ -72,7 +72,7 @@ def engram_gate(x, k, v, wh, we, eps=B.EPS, dsqrt_clamp=B.DSQRT_CLAMP):
 class EngramGate(torch.nn.Module):
     """The gate as a module with its two RMSNorm weights as parameters.
 
-    forward(hidden_states, k, v) -> hidden_states + gate * v, all [..., H] bf16
+    forward(x, k, v) returns x + gate * v; x, k, v are [..., H] bf16
     on the GPU; `last_gate` keeps the most recent per-token gate (fp32)."""
 
     def __init__(self, hidden_size: int, eps: float = B.EPS,
@@ -85,11 +85,10 @@ class EngramGate(torch.nn.Module):
         self.we = torch.nn.Parameter(torch.ones(hidden_size, dtype=torch.float32, device=device))
         self.last_gate = None
 
-    def forward(self, hidden_states, k, v):
-        if hidden_states.shape[-1] != self.hidden_size:
-            raise ValueError(f"last dimension must be {self.hidden_size}, got "
-                             f"{hidden_states.shape[-1]}")
-        out, gate = EngramGateFunction.apply(hidden_states, k, v, self.wh, self.we,
+    def forward(self, x, k, v):
+        if x.shape[-1] != self.hidden_size:
+            raise ValueError(f"last dimension must be {self.hidden_size}, got {x.shape[-1]}")
+        out, gate = EngramGateFunction.apply(x, k, v, self.wh, self.we,
                                              self.eps, self.dsqrt_clamp)
         self.last_gate = gate
         return out

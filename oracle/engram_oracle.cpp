@@ -6,10 +6,11 @@
 // It shares no code with the GPU library.
 //
 // Source of the method: the zhichai.net TileKernels page ("DeepSeek 开源
-// TileKernels ..."), section "5. Engram — 条件记忆门控", gate formula:
-//   gate   = sigmoid(signed_sqrt(dot(RMSNorm(x, wh), RMSNorm(k, we)) * scalar))
-//   output = hidden_states + gate * v
-//   signed_sqrt(x) = sign(x) * sqrt(|x|),  scalar = 1 / sqrt(hidden_size)
+// TileKernels ..."), section "5. Engram — 条件记忆门控", gate formula. In this
+// file's notation, per token with rows x, k, v of width H:
+//   a = RMSNorm of x with weight wh,   b = RMSNorm of k with weight we,
+//   d = sum_i a_i b_i,   z = d / sqrt(H),   s = sign(z) sqrt|z|,
+//   gate = 1 / (1 + exp(-s)),   out = x + gate * v.
 // The same section names the fused forward/backward kernels and a separate
 // weight-gradient reduction; the juejin.cn page (highlight 5) says the
 // autograd wrapper covers forward, backward and weight-gradient reduction.

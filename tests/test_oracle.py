@@ -1,8 +1,9 @@
 """Pins of the fp64 oracle against what the formula itself fixes.
 
 The gate is defined on the zhichai.net TileKernels page, section "5. Engram"
-(gate formula): gate = sigmoid(signed_sqrt(dot(RMSNorm(x, wh), RMSNorm(k, we))
-* scalar)), scalar = 1/sqrt(hidden_size), output = hidden_states + gate * v.
+(gate formula): per token the two RMSNorm outputs of x (weight wh) and k
+(weight we) are dotted, the dot is scaled by 1/sqrt(H), passed through the
+signed square root and a sigmoid to give the gate, and out = x + gate * v.
 The pages print no worked example, so the oracle is pinned by closed forms,
 exact special cases, invariances, a library RMSNorm, and finite differences
 and automatic differentiation of its forward for the backward.
