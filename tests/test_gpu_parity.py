@@ -258,6 +258,39 @@ def test_special_rows(eg, cuda_device):
     assert abs(gate[4] + gate[5] - 1.0) < 2e-6
 
 
+def test_derivative_clamp_region(eg, cuda_device):
+    """Rows whose z sits on both sides of the derivative clamp. x lives on
+    the even columns and k on the odd ones, except k[0] = c: the weighted
+    dot is then the single exact product x[0] c wh[0] we[0], so z is known
+    to fp32 rounding of the two norms and each row lands where it is meant
+    to, below, near or above the clamp."""
+    H = 4096
+    cs = [s * 2.0 ** -e for e in range(4, 15) for s in (1, -1)]
+    T = len(cs)
+
+    def fill(d):
+        d["x"][:, 1::2] = 0
+        d["k"][:, 0::2] = 0
+        d["k"][:, 0] = synth.round_bf16(np.array(cs))
+    d = make_case(T, H, seed=11, fill=fill)
+    _, _, z = oracle.fwd_bf16(d["x"], d["k"], d["v"], d["wh"], d["we"], want_out=False)
+    az = np.abs(z)
+    assert np.sum(az < 0.5 * oracle.CLAMP) >= 4 and np.sum(az > 2 * oracle.CLAMP) >= 4
+    assert np.sum((az > 0.5 * oracle.CLAMP) & (az < 2 * oracle.CLAMP)) >= 2
+    g = run_gpu(eg, d, cuda_device)
+    assert_report(compare(d, g), name="clamp region")
+    assert_dv_is_gate_times_grad(d, g)
+    # row by row as well: a wrong branch on one row would hide in the totals
+    o_dx, o_dk, _, _, _, _ = oracle.bwd_bf16(d["grad_out"], d["x"], d["k"], d["v"],
+                                             d["wh"], d["we"])
+    for name, o in (("dx", o_dx), ("dk", o_dk)):
+        ref = oracle.bf16_to_f64(oracle.round_bf16(o))
+        got = oracle.bf16_to_f64(g[name])
+        rel = np.linalg.norm(got - ref, axis=1) / np.linalg.norm(ref, axis=1)
+        say(f"[clamp region] {name} worst row rel L2 {rel.max():.3e}")
+        assert np.all(rel <= REL_TOL), (name, np.flatnonzero(rel > REL_TOL), z)
+
+
 def test_empty_and_zero_partials(eg, cuda_device):
     import torch
     dev = cuda_device
