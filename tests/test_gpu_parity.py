@@ -190,6 +190,73 @@ def test_full_size(eg, cuda_device, cfg):
     assert_dv_is_gate_times_grad(d, g)
 
 
+@pytest.mark.timeout(900)
+def test_tensors_beyond_2_31_elements(eg, cuda_device):
+    """T * H = 2,150,400,000 > 2^31 (4.3 GB per bf16 tensor): every offset
+    past 2^31 elements must still land on its own row. Each input tensor
+    repeats a seeded tile of rows with its own prime period, so no two of the
+    300,000 tokens share all four input rows, and every element of every
+    output is compared with the oracle, streamed over chunks of rows."""
+    import torch
+    dev = cuda_device
+    H, T = 7168, 300_000
+    assert T * H > 2 ** 31
+    periods = {"x": 4099, "k": 4111, "v": 4127, "grad_out": 4129}
+    r = np.random.default_rng(23)
+    tiles = {n: synth.round_bf16(r.standard_normal((p, H))) for n, p in periods.items()}
+    wh = (1 + 0.1 * r.standard_normal(H)).astype(np.float32)
+    we = (1 + 0.1 * r.standard_normal(H)).astype(np.float32)
+    say(f"[T={T} H={H}] building {T * H * 2 / 1e9:.1f} GB device tensors")
+    ar = torch.arange(T, device=dev)
+    t = {}
+    for n, p in periods.items():
+        tile = to_dev(tiles[n], dev)
+        t[n] = tile[ar % p]
+        del tile
+    del ar
+    whd, wed = torch.from_numpy(wh).to(dev), torch.from_numpy(we).to(dev)
+    out, gate = eg.tk_engram_gate_fwd(t["x"], t["k"], t["v"], whd, wed)
+    dx, dk, dv, ws, P = eg.tk_engram_gate_bwd(t["grad_out"], t["x"], t["k"], t["v"], whd, wed)
+    dwh, dwe = eg.tk_engram_grad_w_reduce(ws, P, H, whd, wed)
+    torch.cuda.synchronize()
+    del t, ws
+    say(f"[T={T} H={H}] GPU done (P={P}), comparing every element with the oracle")
+    gate_h = gate.cpu().numpy()
+    st = {n: oracle.BF16Stats() for n in ("dx", "dk", "dv")}
+    out_res = np.zeros(4)
+    gate_err, min_abs_z = 0.0, np.inf
+    o_dwh, o_dwe = np.zeros(H), np.zeros(H)
+    chunk = 4096
+    for a in range(0, T, chunk):
+        b = min(T, a + chunk)
+        rows = np.arange(a, b)
+        h = {n: tiles[n][rows % p] for n, p in periods.items()}
+        o_out, o_gate, o_z = oracle.fwd_bf16(h["x"], h["k"], h["v"], wh, we)
+        gate_err = max(gate_err, float(np.max(np.abs(gate_h[a:b] - o_gate))))
+        nz = np.abs(o_z[o_z != 0])
+        if nz.size:
+            min_abs_z = min(min_abs_z, float(nz.min()))
+        oracle.check_out(to_host_bits(out[a:b]), o_out, h["x"], h["v"], o_gate, out_res)
+        del o_out
+        o_dx, o_dk, o_dv, p_wh, p_we, _ = oracle.bwd_bf16(h["grad_out"], h["x"], h["k"],
+                                                          h["v"], wh, we)
+        st["dx"].add(to_host_bits(dx[a:b]), o_dx)
+        st["dk"].add(to_host_bits(dk[a:b]), o_dk)
+        st["dv"].add(to_host_bits(dv[a:b]), o_dv)
+        o_dwh += p_wh
+        o_dwe += p_we
+        del o_dx, o_dk, o_dv
+        if (a // chunk) % 16 == 15:
+            say(f"[T={T} H={H}] compared rows < {b}")
+    g_dwh, g_dwe = dwh.cpu().numpy(), dwe.cpu().numpy()
+    rep = {"gate_err": gate_err, "out": out_res, "min_abs_z": min_abs_z, "st": st,
+           "dwh_rel": float(np.linalg.norm(g_dwh - o_dwh) / np.linalg.norm(o_dwh)),
+           "dwe_rel": float(np.linalg.norm(g_dwe - o_dwe) / np.linalg.norm(o_dwe))}
+    del out, gate, dx, dk, dv, dwh, dwe
+    torch.cuda.empty_cache()
+    assert_report(rep, name=f"T={T} H={H}, beyond 2^31 elements")
+
+
 # ------------------------------------------------------------- determinism
 
 def test_reruns_are_bit_identical(eg, cuda_device):
