@@ -1,4 +1,4 @@
-// Host-side sanitizer driver for the C ABI of include/tk_engram.h: every
+// Host-side sanitizer program for the C ABI of include/tk_engram.h: every
 // argument check of every entry point, run without a GPU (each call below
 // returns its status before any device work). Built from the library
 // sources with the host half under -fsanitize=address,undefined by
@@ -83,6 +83,6 @@ int main() {
   EXPECT(tk_engram_stream_probe(srcs, 2, dsts, 5, 64, nullptr), TK_ERR_SHAPE);
   EXPECT(tk_engram_stream_probe(srcs, 2, dsts, 2, 40, nullptr), TK_ERR_ALIGN);
   EXPECT(tk_engram_copy_probe(a, a, 40, nullptr), TK_ERR_ALIGN);
-  std::printf("host ABI driver ok\n");
+  std::printf("host ABI program ok\n");
   return 0;
 }

@@ -1,4 +1,4 @@
-// Host-side sanitizer driver for the test infrastructure's C++: the fp64
+// Host-side sanitizer program for the test infrastructure's C++: the fp64
 // oracle, the comparison helpers, the N-gram hash oracle and the seeded input
 // generator. Built with -fsanitize=address,undefined by
 // tests/test_host_sanitizers.py and run on small inputs; any invalid access
@@ -105,6 +105,6 @@ int main() {
                      0xFFFFFFFFu, idx.data());
   for (size_t i = 0; i < idx.size(); ++i)
     if (idx[i] < 0) return 2;
-  std::printf("host oracle driver ok (%g %g)\n", acc[0], res[0]);
+  std::printf("host oracle program ok (%g %g)\n", acc[0], res[0]);
   return 0;
 }

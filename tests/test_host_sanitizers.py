@@ -35,7 +35,7 @@ def test_oracle_and_generator_under_asan_ubsan(tmp_path):
             os.path.join(ROOT, "synth", "synth.cpp")]
     run(["g++", "-O1", "-g", "-std=c++17", "-pthread", *SAN, *srcs, "-o", exe])
     out = run([exe], env=ENV)
-    assert "host oracle driver ok" in out
+    assert "host oracle program ok" in out
 
 
 def test_c_abi_checks_under_asan_ubsan(tmp_path):
@@ -53,4 +53,4 @@ def test_c_abi_checks_under_asan_ubsan(tmp_path):
          "-I", os.path.join(ROOT, "include"), *srcs,
          os.path.join(HERE, "host_abi_main.cpp"), "-o", exe])
     out = run([exe], env=ENV)
-    assert "host ABI driver ok" in out
+    assert "host ABI program ok" in out
