@@ -176,38 +176,48 @@ def time_hash(eg, dev, name: str = "b1024s4096", reps: int = 20) -> dict:
             "frac": nbytes / (us * 1e3) / HBM_PEAK_GBPS}
 
 
-def time_gather(eg, dev, reps: int = 20) -> dict:
+def time_gather(eg, dev, reps: int = 20) -> tuple:
     """tk_engram_gather on the H=7168 workload's memory read: 32768 tokens, 16
     tables (2 layers x 8) of 2^19 rows x 448 bf16, indices from
-    tk_engram_hash. Algorithmic bytes per (token, table): 4 (index) + 2d
-    (row read) + 2d (row written)."""
+    tk_engram_hash, for uniform token ids and for Zipf(1) token frequencies.
+    Algorithmic bytes per (token, table): 4 (index) + 2d (row read) + 2d (row
+    written); with Zipf tokens some rows repeat and may be served from cache,
+    so that line also states the fraction of distinct rows."""
     import synth
     import torch
-    hc = synth.HASH_CONFIGS["b8s4096"]
     gc = synth.GATHER_CONFIGS["t32768_d448"]
-    p = synth.hash_params(hc)
     stride = 1 << 19
     data = torch.empty((gc.tables * stride, gc.d), dtype=torch.bfloat16, device=dev)
     for q in range(gc.tables):
         synth.fill_table_bits_torch(data, q, q * stride, stride, gc.d)
     off = np.arange(gc.tables, dtype=np.int64) * stride
-    sizes = p["table_size"].reshape(-1)
-    tokens = torch.from_numpy(synth.hash_tokens(hc)).to(dev)
-    idx = eg.tk_engram_hash(tokens, p["ngram"], p["mult"], p["table_size"], p["pad"])
     out = torch.empty((gc.T, gc.tables, gc.d), dtype=torch.bfloat16, device=dev)
-    idx2 = idx.view(gc.T, gc.tables)
+    res = []
+    for recipe in ("b8s4096", "b8s4096_zipf"):
+        hc = synth.HASH_CONFIGS[recipe]
+        p = synth.hash_params(hc)
+        sizes = p["table_size"].reshape(-1)
+        tokens = torch.from_numpy(synth.hash_tokens(hc)).to(dev)
+        idx = eg.tk_engram_hash(tokens, p["ngram"], p["mult"], p["table_size"], p["pad"])
+        idx2 = idx.view(gc.T, gc.tables)
 
-    def call():
-        eg.tk_engram_gather(idx2, data, off, sizes, out)
+        def call():
+            eg.tk_engram_gather(idx2, data, off, sizes, out)
 
-    us = avg_launch_us(call, reps)
-    n = gc.T * gc.tables
-    nbytes = n * (4 + 4 * gc.d)
-    del data, tokens, idx, out, idx2
+        us = avg_launch_us(call, reps)
+        ih = idx2.cpu().numpy()
+        distinct = sum(len(np.unique(ih[:, q])) for q in range(gc.tables))
+        n = gc.T * gc.tables
+        nbytes = n * (4 + 4 * gc.d)
+        res.append({"workload": gc.name + ("_zipf" if hc.zipf else ""), "tokens": gc.T,
+                    "token_ids": "Zipf(1)" if hc.zipf else "uniform",
+                    "rows_gathered": n, "distinct_rows_frac": distinct / n, "us": us,
+                    "tokens_per_s": gc.T / (us / 1e6), "bytes": nbytes,
+                    "GBps": nbytes / (us * 1e3), "frac": nbytes / (us * 1e3) / HBM_PEAK_GBPS})
+        del tokens, idx, idx2
+    del data, out
     torch.cuda.empty_cache()
-    return {"workload": gc.name, "tokens": gc.T, "rows_gathered": n, "us": us,
-            "tokens_per_s": gc.T / (us / 1e6), "bytes": nbytes,
-            "GBps": nbytes / (us * 1e3), "frac": nbytes / (us * 1e3) / HBM_PEAK_GBPS}
+    return res[0], res[1]
 
 
 def copy_ceiling(nbytes: int, eg, dev, reps: int = 20) -> dict:
@@ -441,12 +451,12 @@ def main():
     main_res["fwd"]["frac_of_mix_ceiling"] = main_res["fwd"]["GBps"] / ceilings["fwd_3r1w"]["GBps"]
     main_res["bwd_kernel"]["frac_of_mix_ceiling"] = (main_res["bwd_kernel"]["GBps"]
                                                      / ceilings["bwd_4r3w"]["GBps"])
-    hash_res = gather_res = None
+    hash_res = gather_res = gather_zipf_res = None
     if not args.no_secondary:
         print("[bench] timing the N-gram hash", file=sys.stderr, flush=True)
         hash_res = time_hash(eg, dev)
         print("[bench] timing the hashed gather", file=sys.stderr, flush=True)
-        gather_res = time_gather(eg, dev)
+        gather_res, gather_zipf_res = time_gather(eg, dev)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -485,6 +495,7 @@ def main():
         "mix_ceilings": ceilings,
         "hash": hash_res,
         "gather": gather_res,
+        "gather_zipf": gather_zipf_res,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line))

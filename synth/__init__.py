@@ -270,6 +270,7 @@ class HashConfig:
     table_rows: int      # table sizes are distinct primes just below this
     vocab: int
     describe: str
+    zipf: float = 0.0    # 0: ids uniform over the vocabulary; s > 0: Zipf(s) frequencies
 
 
 HASH_CONFIGS = {
@@ -278,6 +279,10 @@ HASH_CONFIGS = {
     "b8s4096": HashConfig("hash_b8s4096", 8, 4096, (2, 3), 8, 1 << 19, 129280,
                           "batch 8 x seq 4096 = 32768 tokens (the H=7168 gate workload), "
                           "2-gram and 3-gram layers, 8 tables each of ~2^19 rows"),
+    "b8s4096_zipf": HashConfig("hash_b8s4096_zipf", 8, 4096, (2, 3), 8, 1 << 19, 129280,
+                               "batch 8 x seq 4096 = 32768 tokens whose frequencies follow "
+                               "Zipf(1) over the vocabulary, as word frequencies in text do; "
+                               "same layers and tables", zipf=1.0),
     "b64s4096": HashConfig("hash_b64s4096", 64, 4096, (2, 3), 8, 1 << 19, 129280,
                            "batch 64 x seq 4096 = 262144 tokens, same layers and tables"),
     "b1024s4096": HashConfig("hash_b1024s4096", 1024, 4096, (2, 3), 8, 1 << 19, 129280,
@@ -297,11 +302,37 @@ def hash_params(cfg: HashConfig, seed: int = 0) -> dict:
             "table_size": sizes, "pad": cfg.vocab}
 
 
+# Zipf ranks map to ids through r -> (r * ZIPF_ID_STRIDE + ZIPF_ID_SHIFT) mod
+# vocab, a bijection whenever the stride is coprime with the vocabulary size,
+# so the frequent tokens are spread over the id range instead of being the
+# smallest ids.
+ZIPF_ID_STRIDE = 7919
+ZIPF_ID_SHIFT = 17
+
+
+def zipf_ranks(u01: np.ndarray, vocab: int, s: float) -> np.ndarray:
+    """Ranks in [0, vocab) with P(rank = r) proportional to (r + 1)^-s, by
+    inverting the cumulative distribution at the uniforms u01 in [0, 1)."""
+    w = np.arange(1, vocab + 1, dtype=np.float64) ** -s
+    cdf = np.cumsum(w)
+    cdf /= cdf[-1]
+    return np.minimum(np.searchsorted(cdf, u01, side="right"), vocab - 1)
+
+
+def zipf_rank_to_id(rank: np.ndarray, vocab: int) -> np.ndarray:
+    assert np.gcd(ZIPF_ID_STRIDE, vocab) == 1
+    return (np.asarray(rank, dtype=np.int64) * ZIPF_ID_STRIDE + ZIPF_ID_SHIFT) % vocab
+
+
 def hash_tokens(cfg: HashConfig, seed: int = 0) -> np.ndarray:
-    """Token ids int32 [B, S], uniform over the vocabulary (Philox stream)."""
+    """Token ids int32 [B, S] from the Philox stream: uniform over the
+    vocabulary, or with Zipf(cfg.zipf) frequencies when cfg.zipf > 0."""
     n = cfg.B * cfg.S
-    u = uniform_pm1(seed, STREAM_TOKENS, n)          # in [-1, 1)
-    ids = np.floor((u + 1.0) * 0.5 * cfg.vocab).astype(np.int64)
+    u01 = (uniform_pm1(seed, STREAM_TOKENS, n) + 1.0) * 0.5     # in [0, 1)
+    if cfg.zipf > 0:
+        ids = zipf_rank_to_id(zipf_ranks(u01, cfg.vocab, cfg.zipf), cfg.vocab)
+    else:
+        ids = np.floor(u01 * cfg.vocab).astype(np.int64)
     return np.clip(ids, 0, cfg.vocab - 1).astype(np.int32).reshape(cfg.B, cfg.S)
 
 

@@ -78,13 +78,15 @@ def test_gather_shapes(eg, cuda_device, T, Q, d):
 
 
 @pytest.mark.timeout(600)
-def test_memory_read_full_size(eg, cuda_device):
+@pytest.mark.parametrize("tokens_recipe", ["b8s4096", "b8s4096_zipf"])
+def test_memory_read_full_size(eg, cuda_device, tokens_recipe):
     """tokens -> tk_engram_hash -> tk_engram_gather at the H=7168 workload's
-    size (32768 tokens, 16 tables of ~2^19 rows x 448 bf16): every index is
-    compared with the oracle hash, every gathered row with the table
-    pattern recomputed on the host."""
+    size (32768 tokens, 16 tables of ~2^19 rows x 448 bf16), with uniform
+    and with Zipf(1) token frequencies: every index is compared with the
+    oracle hash, every gathered row with the table pattern recomputed on
+    the host."""
     import torch
-    hc = synth.HASH_CONFIGS["b8s4096"]
+    hc = synth.HASH_CONFIGS[tokens_recipe]
     gc = synth.GATHER_CONFIGS["t32768_d448"]
     p = synth.hash_params(hc)
     tokens = synth.hash_tokens(hc)

@@ -25,7 +25,7 @@ def gpu_hash(eg, dev, tokens, ngram, mult, table_size, pad):
     return out.cpu().numpy()
 
 
-@pytest.mark.parametrize("name", ["tiny", "b8s4096", "b64s4096"])
+@pytest.mark.parametrize("name", ["tiny", "b8s4096", "b8s4096_zipf", "b64s4096"])
 def test_hash_workloads(eg, cuda_device, name):
     c = synth.HASH_CONFIGS[name]
     p = synth.hash_params(c)

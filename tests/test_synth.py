@@ -109,3 +109,35 @@ def test_stress_row_classes():
     big = synth.student_t3_bf16(0, synth.STREAM_V, 64, 4096, np.ones(64))
     bf = synth.bf16_to_f64(big)
     assert 2.0 < bf.var() < 4.5 and abs(np.median(bf)) < 0.02
+
+
+def test_zipf_ranks_small_vocabulary_exact():
+    # vocab 4, s = 1: weights 1, 1/2, 1/3, 1/4 (sum 25/12), so the CDF is
+    # 12/25, 18/25, 22/25, 1; uniforms just below and just above each step
+    # land on either side of it
+    cuts = np.array([12, 18, 22]) / 25
+    u = np.concatenate([cuts - 1e-12, cuts + 1e-12, [0.0, 0.999999]])
+    assert synth.zipf_ranks(u, 4, 1.0).tolist() == [0, 1, 2, 1, 2, 3, 0, 3]
+
+
+def test_zipf_id_map_is_a_bijection():
+    V = synth.HASH_CONFIGS["b8s4096_zipf"].vocab
+    ids = synth.zipf_rank_to_id(np.arange(V), V)
+    assert ids.min() == 0 and ids.max() == V - 1 and len(np.unique(ids)) == V
+
+
+def test_zipf_token_frequencies():
+    c = synth.HASH_CONFIGS["b8s4096_zipf"]
+    t = synth.hash_tokens(c).ravel()
+    assert np.array_equal(t, synth.hash_tokens(c).ravel())           # seeded
+    assert t.min() >= 0 and t.max() < c.vocab
+    n = t.size
+    harmonic = np.sum(1.0 / np.arange(1, c.vocab + 1))
+    for r in range(4):
+        p = 1.0 / ((r + 1) * harmonic)
+        tok = int(synth.zipf_rank_to_id(r, c.vocab))
+        cnt = int(np.sum(t == tok))
+        assert abs(cnt - n * p) < 5 * np.sqrt(n * p * (1 - p)), (r, cnt, n * p)
+    # the uniform recipe stays uniform: no id carries more than a few tokens
+    u = synth.hash_tokens(synth.HASH_CONFIGS["b8s4096"]).ravel()
+    assert np.bincount(u, minlength=c.vocab).max() < 10
