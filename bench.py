@@ -152,6 +152,54 @@ def time_workload(w: Workload, steps: int, warmup: int) -> dict:
     }
 
 
+def time_autograd(w: Workload, eg, steps: int, warmup: int, raw_ms: float) -> dict:
+    """The autograd wrapper (EngramGate) on a workload's tensors: forward, then
+    backward with fresh .grad tensors each step (set to None first, as
+    zero_grad(set_to_none=True) does); HIP events on torch's current stream.
+    The outputs and gradients come from torch's caching allocator."""
+    import torch
+    layer = eg.EngramGate(w.H, device=w.x.device)
+    with torch.no_grad():
+        layer.wh.copy_(w.wh)
+        layer.we.copy_(w.we)
+    x, k, v = (t.detach().requires_grad_() for t in (w.x, w.k, w.v))
+    leaves = (x, k, v, layer.wh, layer.we)
+
+    def step():
+        for t in leaves:
+            t.grad = None
+        layer(x, k, v).backward(w.g)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        step()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    for t in leaves:
+        t.grad = None
+    del layer, x, k, v, leaves
+    return {"workload": w.c.name, "steps": steps, "ms_per_step": ms,
+            "tokens_per_s": w.T / (ms / 1e3), "vs_c_abi_step": raw_ms / ms}
+
+
+def time_fused_weight(eg, dev, H: int, reps: int = 50) -> dict:
+    """tk_engram_fused_weight at width H: 8 bytes read and 8 written per
+    element; at these widths one launch is a few microseconds of latency."""
+    import torch
+    g = torch.Generator().manual_seed(0)
+    wh = (1 + 0.1 * torch.randn(H, generator=g)).to(dev)
+    we = (1 + 0.1 * torch.randn(H, generator=g)).to(dev)
+    w = torch.empty((H,), dtype=torch.float64, device=dev)
+    us = avg_launch_us(eg.bind_fused_weight(wh, we, w), reps)
+    return {"H": H, "us": us, "bytes": 16 * H}
+
+
 def time_hash(eg, dev, name: str = "b1024s4096", reps: int = 20) -> dict:
     """tk_engram_hash throughput on a large batch: average launch time from HIP
     events over back-to-back launches; algorithmic bytes = 4 per token read
@@ -417,6 +465,10 @@ def main():
     w = Workload(args.workload, dev, eg)
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
     main_res = time_workload(w, args.steps, args.warmup)
+    autograd_res = None
+    if not args.no_secondary:
+        print("[bench] timing the autograd wrapper", file=sys.stderr, flush=True)
+        autograd_res = time_autograd(w, eg, min(args.steps, 20), 3, main_res["ms_per_step"])
     host = w.host
     w.free()
     torch.cuda.empty_cache()
@@ -451,12 +503,13 @@ def main():
     main_res["fwd"]["frac_of_mix_ceiling"] = main_res["fwd"]["GBps"] / ceilings["fwd_3r1w"]["GBps"]
     main_res["bwd_kernel"]["frac_of_mix_ceiling"] = (main_res["bwd_kernel"]["GBps"]
                                                      / ceilings["bwd_4r3w"]["GBps"])
-    hash_res = gather_res = gather_zipf_res = None
+    hash_res = gather_res = gather_zipf_res = fused_res = None
     if not args.no_secondary:
         print("[bench] timing the N-gram hash", file=sys.stderr, flush=True)
         hash_res = time_hash(eg, dev)
         print("[bench] timing the hashed gather", file=sys.stderr, flush=True)
         gather_res, gather_zipf_res = time_gather(eg, dev)
+        fused_res = time_fused_weight(eg, dev, main_res["H"])
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -495,6 +548,8 @@ def main():
         "mix_ceilings": ceilings,
         "hash": hash_res,
         "gather": gather_res,
+        "autograd": autograd_res,
+        "fused_weight": fused_res,
         "gather_zipf": gather_zipf_res,
         "cpu_baseline": cpu,
     }

@@ -12,6 +12,7 @@ same names and only marshal torch tensors into it.
 from ._binding import (  # noqa: F401
     DSQRT_CLAMP,
     BoundCall,
+    bind_fused_weight,
     bind_gate_bwd,
     bind_gate_fwd,
     bind_grad_w_reduce,

@@ -367,6 +367,20 @@ def tk_engram_gather(idx, table_data, row_offset, rows, out=None, stream=None):
     return out
 
 
+def bind_fused_weight(wh, we, w, stream=None):
+    """tk_engram_fused_weight with fixed arguments; see tk_engram_fused_weight."""
+    torch = _torch()
+    if not isinstance(wh, torch.Tensor) or wh.dim() != 1 or wh.device.type != "cuda":
+        raise ValueError("wh must be a 1-D fp32 GPU tensor")
+    H = wh.shape[0]
+    dev = wh.device
+    args = [_need(wh, "wh", torch.float32, (H,), dev), _need(we, "we", torch.float32, (H,), dev),
+            _need(w, "w", torch.float64, (H,), dev), ctypes.c_int64(H),
+            _stream_handle(dev, stream)]
+    return BoundCall("tk_engram_fused_weight", load_library().tk_engram_fused_weight, args,
+                     (wh, we, w))
+
+
 def tk_engram_fused_weight(wh, we, w=None, stream=None):
     """w = wh * we in fp64 (exact), from fp32 [H] GPU tensors."""
     torch = _torch()

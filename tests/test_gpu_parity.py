@@ -420,10 +420,14 @@ def test_fused_weight_is_the_exact_product(eg, cuda_device, H):
     r = np.random.default_rng(H)
     wh = (1 + 0.1 * r.standard_normal(H)).astype(np.float32)
     we = (r.standard_normal(H) * 10.0 ** r.integers(-30, 30, H)).astype(np.float32)
-    w = eg.tk_engram_fused_weight(torch.from_numpy(wh).to(cuda_device),
-                                  torch.from_numpy(we).to(cuda_device))
+    whd, wed = torch.from_numpy(wh).to(cuda_device), torch.from_numpy(we).to(cuda_device)
+    w = eg.tk_engram_fused_weight(whd, wed)
+    w2 = torch.full((H,), float("nan"), dtype=torch.float64, device=cuda_device)
+    eg.bind_fused_weight(whd, wed, w2)()                  # the pre-marshalled form
     torch.cuda.synchronize()
-    assert np.array_equal(w.cpu().numpy(), oracle.fused_weight(wh, we))
+    want = oracle.fused_weight(wh, we)
+    assert np.array_equal(w.cpu().numpy(), want)
+    assert np.array_equal(w2.cpu().numpy(), want)
 
 
 # ----------------------------------------------------------------- HIP graphs
