@@ -254,6 +254,18 @@ struct RowWalk {
   }
 };
 
+// The workgroup's logical number b in the walk above. The dispatcher hands
+// workgroups to the 8 XCDs in turn (hardware workgroup w runs on XCD w mod 8),
+// so numbering them XCD by XCD gives each XCD a contiguous slab of the rows
+// in flight instead of every 8th row; the backward at H = 7168 gains about
+// 1%. It is a fixed permutation of the grid, so which rows and which partial
+// slot belong to logical block b, and hence every result bit, are unchanged.
+// Grids that 8 does not divide keep the plain numbering.
+__device__ __forceinline__ int64_t xcd_slab_block() {
+  const int64_t w = blockIdx.x, G = gridDim.x;
+  return (G & 7) ? w : (w & 7) * (G >> 3) + (w >> 3);
+}
+
 // ---- forward ---------------------------------------------------------------
 
 template <int C>
@@ -345,7 +357,8 @@ __global__ __launch_bounds__(W * kWave) void gate_fwd_kernel(
   __shared__ float red_f[2][2][W];
   __shared__ double red_d[2][W];
 
-  const int64_t first = (int64_t)blockIdx.x * walk.block_stride;
+  const int64_t blk = xcd_slab_block();
+  const int64_t first = blk * walk.block_stride;
   const int64_t n = walk.rows_of(first);
   if (n <= 0) return;
   const int64_t step = walk.row_step;
@@ -495,7 +508,8 @@ __global__ __launch_bounds__(W * kWave) void gate_bwd_kernel(
 #pragma unroll
     for (int e = 0; e < 8; ++e) cacc[j][e] = 0.f;
 
-  const int64_t first = (int64_t)blockIdx.x * walk.block_stride;
+  const int64_t blk = xcd_slab_block();
+  const int64_t first = blk * walk.block_stride;
   const int64_t n = walk.rows_of(first);
 
   if (n > 0) {
@@ -534,7 +548,7 @@ __global__ __launch_bounds__(W * kWave) void gate_bwd_kernel(
   }
 
   // This block's partial row of c.
-  f32x4* prow = partial + (int64_t)blockIdx.x * (2 * nchunk);
+  f32x4* prow = partial + blk * (2 * nchunk);
 #pragma unroll
   for (int j = 0; j < C; ++j) {
     const int c = j * NT + tid;
