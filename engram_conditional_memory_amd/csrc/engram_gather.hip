@@ -12,9 +12,13 @@
 //
 // One workgroup per token: its Q rows are Q * d / 8 16-byte chunks, written
 // to a contiguous stretch of `out`; each thread moves up to four chunks at a
-// time (all four loads issued before the stores). Table reads are plain
-// loads (common N-grams repeat, so rows can be re-used from cache); the
-// output is streamed with nontemporal stores.
+// time (all four loads issued before the stores). The token's Q indices are
+// staged in LDS by one load, and each thread works out where its chunks live
+// while that load is in flight, so the row loads issue right after one
+// barrier instead of each waiting on a global index fetch of its own; that
+// takes a memory round trip out of every chunk's dependency chain. Table
+// reads are plain loads (common N-grams repeat, so rows can be re-used from
+// cache); the output is streamed with nontemporal stores.
 
 #include <hip/hip_runtime.h>
 
@@ -28,6 +32,8 @@ namespace {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kGatherBlock = 256;
+static_assert(kGatherBlock >= TK_ENGRAM_GATHER_MAX_TABLES,
+              "one thread per table stages the token's indices");
 constexpr int kGatherUnroll = 4;
 
 struct GatherParams {
@@ -40,29 +46,46 @@ struct GatherParams {
 __global__ __launch_bounds__(kGatherBlock) void gather_kernel(
     const int32_t* __restrict__ idx, const u32x4* __restrict__ table,
     GatherParams p, u32x4* __restrict__ out) {
+  __shared__ int32_t sidx[TK_ENGRAM_GATHER_MAX_TABLES];
   const int64_t t = blockIdx.x;
   const int n = p.tables * p.cpr;
-  const int32_t* ti = idx + t * p.tables;
+  if (threadIdx.x < p.tables) sidx[threadIdx.x] = idx[t * p.tables + threadIdx.x];
+
+  // Where this thread's next kGatherUnroll chunks come from: table q, the
+  // chunk's offset within the packed buffer at row 0 of that table, and the
+  // table's row count (0 for a chunk past the token's end, which then reads
+  // nothing). The first group is located while the index load is in flight.
+  int q[kGatherUnroll];
+  int64_t base[kGatherUnroll];
+  uint32_t lim[kGatherUnroll];
+  auto locate = [&](int j0) {
+#pragma unroll
+    for (int u = 0; u < kGatherUnroll; ++u) {
+      const int j = j0 + u * kGatherBlock;
+      const int qq = j < n ? j / p.cpr : 0;
+      q[u] = qq;
+      base[u] = p.row_offset[qq] * p.cpr + (j - qq * p.cpr);
+      lim[u] = j < n ? p.rows[qq] : 0u;
+    }
+  };
+  locate(threadIdx.x);
+  __syncthreads();
+
   u32x4* to = out + t * n;
   for (int j0 = threadIdx.x; j0 < n; j0 += kGatherUnroll * kGatherBlock) {
     u32x4 v[kGatherUnroll];
 #pragma unroll
     for (int u = 0; u < kGatherUnroll; ++u) {
-      const int j = j0 + u * kGatherBlock;
+      const int32_t i = sidx[q[u]];
       v[u] = u32x4{0u, 0u, 0u, 0u};
-      if (j < n) {
-        const int q = j / p.cpr;
-        const int col = j - q * p.cpr;
-        const int32_t i = ti[q];
-        if (i >= 0 && (uint32_t)i < p.rows[q])
-          v[u] = table[(p.row_offset[q] + i) * p.cpr + col];
-      }
+      if (i >= 0 && (uint32_t)i < lim[u]) v[u] = table[base[u] + (int64_t)i * p.cpr];
     }
 #pragma unroll
     for (int u = 0; u < kGatherUnroll; ++u) {
       const int j = j0 + u * kGatherBlock;
       if (j < n) __builtin_nontemporal_store(v[u], to + j);
     }
+    if (j0 + kGatherUnroll * kGatherBlock < n) locate(j0 + kGatherUnroll * kGatherBlock);
   }
 }
 
