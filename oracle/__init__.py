@@ -23,6 +23,9 @@ _SRC = os.path.join(_HERE, "engram_oracle.cpp")
 _SRC_CMP = os.path.join(_HERE, "compare.cpp")
 _SRC_HASH = os.path.join(_HERE, "engram_hash_oracle.cpp")
 _LIB = os.path.join(_HERE, "liboracle.so")
+# The mutation test plants mistakes in a copy of the sources and points this
+# variable at the copy's library, to show that the pins catch each mistake.
+LIB_OVERRIDE_ENV = "TK_ENGRAM_ORACLE_LIB"
 
 EPS = 1e-6          # RMSNorm epsilon used throughout (the pages give none)
 CLAMP = 1e-4        # lower clamp of |z| in the signed-sqrt derivative
@@ -44,9 +47,10 @@ _lib = None
 def lib() -> ctypes.CDLL:
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB):
-            raise RuntimeError(f"{_LIB} is missing: run __graft_entry__.build()")
-        L = ctypes.CDLL(_LIB)
+        path = os.environ.get(LIB_OVERRIDE_ENV) or _LIB
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: run __graft_entry__.build()")
+        L = ctypes.CDLL(path)
         vp, i64, dbl, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_double, ctypes.c_int
         L.oracle_fwd_f64.argtypes = [vp, vp, vp, vp, vp, i64, i64, dbl, vp, vp, vp]
         L.oracle_bwd_f64.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, dbl, dbl,
