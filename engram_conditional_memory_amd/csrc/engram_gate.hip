@@ -7,12 +7,14 @@
 //
 // Everything on this path streams bf16 rows from HBM and reduces each row to
 // a handful of scalars; nothing is a dense contraction, so no matrix cores
-// are used. Each kernel is built around one idea: a workgroup of W waves owns
-// a contiguous block of rows and walks it one row at a time; the row is split
-// across the W*64 threads in 16-byte chunks (8 bf16), thread `tid` owning
-// chunks tid, tid + W*64, ... so that every load and store instruction of a
-// wave covers 1 KiB of contiguous memory. While a row is reduced and written,
-// the loads of the next row are already in flight.
+// are used. Each kernel is built around one idea: about one workgroup of W
+// waves per CU walks the rows b, b + G, b + 2G, ... (G workgroups, b its
+// logical number) one row at a time, so the rows in flight across the chip
+// stay in one sliding window of the tensors; the row is split across the
+// W*64 threads in 16-byte chunks (8 bf16), thread `tid` owning chunks tid,
+// tid + W*64, ... so that every load and store instruction of a wave covers
+// 1 KiB of contiguous memory. While a row is reduced and written, the loads
+// of the next rows are already in flight.
 //
 // Algebra used by both passes. With w_i = wh_i * we_i (the product of the
 // two RMSNorm weights),

@@ -85,8 +85,8 @@ tk_status tk_engram_gate_fwd(const uint16_t* x, const uint16_t* k,
 
 /*
  * Number of weight-gradient partial rows P the backward writes for (T, H):
- * the tokens are cut into P contiguous blocks, each reduced by one
- * workgroup. A pure function of (T, H); 0 when T = 0.
+ * partial row p sums the tokens t = p, p + P, p + 2P, ... (one workgroup
+ * each). A pure function of (T, H), at most T; 0 when T = 0.
  */
 int64_t tk_engram_num_partials(int64_t T, int64_t H);
 
@@ -101,8 +101,8 @@ size_t tk_engram_bwd_workspace_bytes(int64_t T, int64_t H);
  *   grad_out        : bf16 [T, H]  dL/d out
  *   x, k, v, wh, we : as for the forward
  *   dx, dk, dv      : bf16 [T, H]  dL/dx, dL/dk, dL/dv
- *   workspace       : fp32 [P, H]  per-block weight-gradient partials
- *                     c_p[i] = sum over the block's tokens t of
+ *   workspace       : fp32 [P, H]  weight-gradient partials
+ *                     c_p[i] = sum over the tokens t = p, p + P, ... of
  *                              dd_t * r_x,t * r_k,t * x_t,i * k_t,i
  *                     with dd_t = dL/dd_t; input to tk_engram_grad_w_reduce
  *   workspace_bytes : size of `workspace`, at least

@@ -358,6 +358,34 @@ def test_derivative_clamp_region(eg, cuda_device):
         assert np.all(rel <= REL_TOL), (name, np.flatnonzero(rel > REL_TOL), z)
 
 
+@pytest.mark.parametrize("T,H", [(1000, 4096), (500, 7168), (37, 256)])
+def test_workspace_holds_the_documented_partials(eg, cuda_device, T, H):
+    """The header's contract for the backward's workspace: partial row p is
+    c_p[i] = sum over t = p, p + P, ... of dd_t r_x,t r_k,t x_t,i k_t,i,
+    rebuilt here in fp64 from the oracle's per-token scalars."""
+    import torch
+    d = make_case(T, H, seed=T + H)
+    dev = cuda_device
+    x, k, v = to_dev(d["x"], dev), to_dev(d["k"], dev), to_dev(d["v"], dev)
+    g = to_dev(d["grad_out"], dev)
+    wh, we = torch.from_numpy(d["wh"]).to(dev), torch.from_numpy(d["we"]).to(dev)
+    _, _, _, ws, P = eg.tk_engram_gate_bwd(g, x, k, v, wh, we)
+    torch.cuda.synchronize()
+    assert P == eg.tk_engram_num_partials(T, H) and 1 <= P <= T
+    got = ws.cpu().numpy()[:P]
+    xf, kf = oracle.bf16_to_f64(d["x"]), oracle.bf16_to_f64(d["k"])
+    _, _, fst = oracle.fwd_f64(xf, kf, oracle.bf16_to_f64(d["v"]), d["wh"], d["we"])
+    _, _, _, _, _, dd = oracle.bwd_bf16(d["grad_out"], d["x"], d["k"], d["v"], d["wh"],
+                                        d["we"], want_grads=False)
+    A = dd * fst[:, 2] * fst[:, 3]                    # dd r_x r_k per token
+    want = np.zeros((P, H))
+    for t in range(T):
+        want[t % P] += A[t] * xf[t] * kf[t]
+    rel = np.linalg.norm(got - want) / np.linalg.norm(want)
+    say(f"[workspace T={T} H={H} P={P}] rel L2 {rel:.3e}")
+    assert rel <= 1e-5
+
+
 def test_empty_and_zero_partials(eg, cuda_device):
     import torch
     dev = cuda_device
