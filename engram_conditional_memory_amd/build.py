@@ -9,7 +9,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SRCS = [os.path.join(PKG, "csrc", "engram_gate.hip"),
         os.path.join(PKG, "csrc", "engram_hash.hip"),
-        os.path.join(PKG, "csrc", "engram_gather.hip")]
+        os.path.join(PKG, "csrc", "engram_gather.hip"),
+        os.path.join(PKG, "csrc", "engram_status.cpp")]
 LIB = os.path.join(PKG, "libtk_engram.so")
 INCLUDE = os.path.join(ROOT, "include")
 

@@ -823,22 +823,6 @@ tk_status dispatch_bwd(const Plan& p, const BwdArgs& a, int grid, hipStream_t st
 
 extern "C" {
 
-int32_t tk_abi_version(void) { return TK_ENGRAM_ABI_VERSION; }
-
-const char* tk_status_string(tk_status s) {
-  switch (s) {
-    case TK_SUCCESS: return "success";
-    case TK_ERR_NULL: return "a required pointer is NULL";
-    case TK_ERR_SHAPE: return "invalid shape (T < 0, H <= 0 or P < 0)";
-    case TK_ERR_ALIGN: return "H is not a multiple of 8 or a pointer is not 16-byte aligned";
-    case TK_ERR_UNSUPPORTED: return "H exceeds the supported maximum (8192)";
-    case TK_ERR_WORKSPACE: return "backward workspace is smaller than required";
-    case TK_ERR_LAUNCH: return "kernel launch failed";
-    case TK_ERR_VALUE: return "a scalar or table parameter is out of range";
-    default: return "unknown status";
-  }
-}
-
 int64_t tk_engram_num_partials(int64_t T, int64_t H) {
   if (check_shape(T, H) != TK_SUCCESS) return 0;
   return grid_of(bwd_plan((int)(H / 8)), T);

@@ -57,9 +57,9 @@ typedef int32_t tk_status;
 enum {
   TK_SUCCESS = 0,
   TK_ERR_NULL = 1,        /* a required pointer is NULL                     */
-  TK_ERR_SHAPE = 2,       /* T < 0, H <= 0, or P inconsistent               */
-  TK_ERR_ALIGN = 3,       /* H not a multiple of 8 or a pointer misaligned  */
-  TK_ERR_UNSUPPORTED = 4, /* H above the supported maximum                  */
+  TK_ERR_SHAPE = 2,       /* negative count, width <= 0, P inconsistent    */
+  TK_ERR_ALIGN = 3,       /* width not a multiple of 8, pointer misaligned */
+  TK_ERR_UNSUPPORTED = 4, /* a size above the call's supported maximum      */
   TK_ERR_WORKSPACE = 5,   /* backward workspace smaller than required       */
   TK_ERR_LAUNCH = 6,      /* the HIP runtime refused the kernel launch      */
   TK_ERR_VALUE = 7        /* a scalar or table parameter is out of range    */

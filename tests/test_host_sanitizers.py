@@ -44,7 +44,7 @@ def test_c_abi_checks_under_asan_ubsan(tmp_path):
     exe = str(tmp_path / "host_abi")
     pkg = os.path.join(ROOT, "engram_conditional_memory_amd", "csrc")
     srcs = [os.path.join(pkg, f) for f in ("engram_gate.hip", "engram_hash.hip",
-                                           "engram_gather.hip")]
+                                           "engram_gather.hip", "engram_status.cpp")]
     host_san = []
     for flag in SAN:
         host_san += ["-Xarch_host", flag]
