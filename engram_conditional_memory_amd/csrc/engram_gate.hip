@@ -721,12 +721,18 @@ Plan generic_plan(int nchunk) {
 Plan fwd_plan(int nchunk) {
   if (nchunk == 896) return {7, 2, 2, true, false, 224};   // H = 7168
   if (nchunk == 512) return {4, 2, 2, true, false, 256};   // H = 4096
+  if (nchunk == 640) return {5, 2, 2, true, false, 256};   // H = 5120
+  if (nchunk == 384) return {3, 2, 3, true, false, 256};   // H = 3072
+  if (nchunk == 256) return {2, 2, 2, true, false, 512};   // H = 2048
   return generic_plan(nchunk);
 }
 
 Plan bwd_plan(int nchunk) {
   if (nchunk == 896) return {7, 2, 3, true, true, 224};    // H = 7168
   if (nchunk == 512) return {4, 2, 2, true, false, 256};   // H = 4096
+  if (nchunk == 640) return {5, 2, 2, true, false, 256};   // H = 5120
+  if (nchunk == 384) return {3, 2, 2, true, false, 256};   // H = 3072
+  if (nchunk == 256) return {2, 2, 3, true, false, 256};   // H = 2048
   return generic_plan(nchunk);
 }
 
@@ -768,6 +774,9 @@ tk_status run_fwd(FwdArgs a, int grid, hipStream_t st) {
 tk_status dispatch_fwd(const Plan& p, const FwdArgs& a, int grid, hipStream_t st) {
   if (p.W == 7 && p.C == 2 && p.full && p.D == 2) return run_fwd<7, 2, true, 2>(a, grid, st);
   if (p.W == 4 && p.C == 2 && p.full && p.D == 2) return run_fwd<4, 2, true, 2>(a, grid, st);
+  if (p.W == 5 && p.C == 2 && p.full && p.D == 2) return run_fwd<5, 2, true, 2>(a, grid, st);
+  if (p.W == 3 && p.C == 2 && p.full && p.D == 3) return run_fwd<3, 2, true, 3>(a, grid, st);
+  if (p.W == 2 && p.C == 2 && p.full && p.D == 2) return run_fwd<2, 2, true, 2>(a, grid, st);
   if (p.D == 2 && p.C == 1) {
     switch (p.W) {
       case 1: return run_fwd<1, 1, false, 2>(a, grid, st);
@@ -805,6 +814,12 @@ tk_status dispatch_bwd(const Plan& p, const BwdArgs& a, int grid, hipStream_t st
     return run_bwd<7, 2, true, 3, true>(a, grid, st);
   if (p.W == 4 && p.C == 2 && p.full && p.D == 2 && !p.wlds)
     return run_bwd<4, 2, true, 2, false>(a, grid, st);
+  if (p.W == 5 && p.C == 2 && p.full && p.D == 2 && !p.wlds)
+    return run_bwd<5, 2, true, 2, false>(a, grid, st);
+  if (p.W == 3 && p.C == 2 && p.full && p.D == 2 && !p.wlds)
+    return run_bwd<3, 2, true, 2, false>(a, grid, st);
+  if (p.W == 2 && p.C == 2 && p.full && p.D == 3 && !p.wlds)
+    return run_bwd<2, 2, true, 3, false>(a, grid, st);
   if (p.D == 2 && !p.wlds && p.C == 1) {
     switch (p.W) {
       case 1: return run_bwd<1, 1, false, 2, false>(a, grid, st);

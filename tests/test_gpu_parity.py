@@ -505,12 +505,14 @@ def test_graph_capture_and_replay(eg, cuda_device):
             assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), i
 
 
-# ------------------------------------------------ untuned widths at volume
+# ------------------------------------------------ other widths at volume
 
-@pytest.mark.parametrize("T,H", [(20001, 3072), (8192, 8192)])
-def test_untuned_widths_many_rows_per_block(eg, cuda_device, T, H):
-    # the generic plans (masked tail chunks at H=3072; 8 waves x 2 chunks at
-    # H=8192) with ~30-80 rows per workgroup, compared on every element
+@pytest.mark.parametrize("T,H", [(20001, 3072), (8192, 8192), (24001, 2048), (9001, 5120),
+                                 (6001, 6144)])
+def test_other_widths_many_rows_per_block(eg, cuda_device, T, H):
+    # the plans of the other widths (H=2048, 3072, 5120: full rows on 2, 3, 5
+    # waves; H=6144: masked tail chunks on 8 waves; H=8192: 8 waves x 2
+    # chunks) with ~25-80 rows per workgroup, compared on every element
     d = make_case(T, H, seed=T + H)
     g = run_gpu(eg, d, cuda_device)
     assert_report(compare(d, g), name=f"T={T} H={H}")
