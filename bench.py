@@ -200,6 +200,42 @@ def time_fused_weight(eg, dev, H: int, reps: int = 50) -> dict:
     return {"H": H, "us": us, "bytes": 16 * H}
 
 
+WIDTHS = (2048, 3072, 4096, 5120, 6144, 7168, 8192)
+
+
+def time_widths(eg, dev, reps: int = 30) -> list:
+    """Forward and backward kernels at every width with a launch plan of its
+    own, and at 6144 and 8192 (generic plans), each on about 470 MB per bf16
+    tensor (T = 235 Mi / H), past the 256 MB Infinity Cache. Inputs are
+    seeded normals; HIP events over back-to-back bound calls."""
+    import torch
+    res = []
+    for H in WIDTHS:
+        T = (235 * 1024 * 1024) // H
+        print(f"[bench] width H={H} T={T}", file=sys.stderr, flush=True)
+        g = torch.Generator(device=dev).manual_seed(H)
+
+        def mk():
+            return torch.randn((T, H), device=dev, generator=g).to(torch.bfloat16)
+
+        x, k, v, go = mk(), mk(), mk(), mk()
+        wh = 1 + 0.1 * torch.randn(H, device=dev, generator=g)
+        we = 1 + 0.1 * torch.randn(H, device=dev, generator=g)
+        out, gate = torch.empty_like(x), torch.empty(T, device=dev)
+        dx, dk, dv = torch.empty_like(x), torch.empty_like(x), torch.empty_like(x)
+        P = eg.tk_engram_num_partials(T, H)
+        ws = torch.empty((P, H), device=dev)
+        f_us = avg_launch_us(eg.bind_gate_fwd(x, k, v, wh, we, out, gate), reps)
+        b_us = avg_launch_us(eg.bind_gate_bwd(go, x, k, v, wh, we, dx, dk, dv, ws), reps)
+        ab = algorithmic_bytes(T, H)
+        res.append({"H": H, "T": T, "P": P,
+                    "fwd_us": f_us, "fwd_frac": ab["fwd"] / (f_us * 1e3) / HBM_PEAK_GBPS,
+                    "bwd_us": b_us, "bwd_frac": ab["bwd"] / (b_us * 1e3) / HBM_PEAK_GBPS})
+        del x, k, v, go, out, gate, dx, dk, dv, ws
+        torch.cuda.empty_cache()
+    return res
+
+
 def time_hash(eg, dev, name: str = "b1024s4096", reps: int = 20) -> dict:
     """tk_engram_hash throughput on a large batch: average launch time from HIP
     events over back-to-back launches; algorithmic bytes = 4 per token read
@@ -442,6 +478,9 @@ def main():
     ap.add_argument("--no-secondary", action="store_true",
                     help="skip the other workloads (second width, stress, small forward, "
                          "memory read)")
+    ap.add_argument("--widths", action="store_true",
+                    help="instead of the default run, time the forward and backward kernels "
+                         "at H = " + ", ".join(map(str, WIDTHS)) + " (one JSON line each)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="summarise two rocprofv3 --pmc runs instead of benchmarking")
     args = ap.parse_args()
@@ -460,6 +499,11 @@ def main():
     import engram_conditional_memory_amd as eg
     eg.load_library()
     dev = torch.device("cuda:0")
+
+    if args.widths:
+        for r in time_widths(eg, dev):
+            print(json.dumps(r))
+        return
 
     print(f"[bench] generating workload {args.workload}", file=sys.stderr, flush=True)
     w = Workload(args.workload, dev, eg)
