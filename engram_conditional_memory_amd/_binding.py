@@ -354,7 +354,11 @@ def tk_engram_gather(idx, table_data, row_offset, rows, out=None, stream=None):
     dev = idx.device
     row_offset = _host_array(row_offset, np.int64, (Q,), "row_offset")
     rows = _host_array(rows, np.uint32, (Q,), "rows")
-    idx2 = idx.reshape(T, Q)
+    if not idx.is_contiguous():
+        # no hidden copy: a temporary freed on return could still be in use
+        # by the kernel on a side stream
+        raise ValueError("idx must be contiguous")
+    idx2 = idx.view(T, Q)
     if out is None:
         out = torch.empty((*lead, Q, d), dtype=torch.bfloat16, device=dev)
     ip = _need(idx2, "idx", torch.int32, (T, Q), dev)

@@ -125,3 +125,17 @@ def test_memory_read_tiny_against_oracles(eg, cuda_device):
     idx = oracle.engram_hash(tokens, p["ngram"], p["mult"], p["table_size"], p["pad"])
     want = oracle.engram_gather(idx.reshape(-1, len(sizes)), bits(data), off, sizes)
     assert np.array_equal(bits(out).reshape(want.shape), want)
+
+
+def test_gather_rejects_a_non_contiguous_index_tensor(eg, cuda_device):
+    import torch
+    rows = np.array([5, 5], dtype=np.uint32)
+    data, off = packed_tables(cuda_device, 2, rows, 8)
+    idx = torch.zeros((2, 4), dtype=torch.int32, device=cuda_device)[:, ::2]
+    assert not idx.is_contiguous()
+    with pytest.raises(ValueError, match="contiguous"):
+        eg.tk_engram_gather(idx, data, off, rows)
+    out = eg.tk_engram_gather(idx.contiguous(), data, off, rows)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(out), oracle.engram_gather(np.zeros((2, 2), np.int32),
+                                                          bits(data), off, rows))
