@@ -7,10 +7,16 @@ all on the same stream, inputs already resident in HBM.
 Prints one JSON line: fwd+bwd tokens/s on the main workload, the roofline of
 the dominant kernel (HBM-bound; algorithmic bytes / average launch time from
 HIP events on the launch stream against 8 TB/s), the same figures for the
-other tuned width, a 128-bit tiled copy as the practical HBM ceiling, and the
+other tuned width and the stress workload, the 1024-token forward hot and
+after a cache scrub, a 128-bit tiled copy and the read/write-mix probes as
+practical HBM ceilings, the N-gram hash and the table gather (uniform and
+Zipf(1) token ids), the autograd module's step, the fused weight, and the
 fp64 oracle's throughput on the host as a reported CPU baseline.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 4]
+
+With --widths it instead times the forward and backward kernels at every
+planned width (one JSON line per width).
 
 With --traffic-from FETCH_CSV WRITE_CSV it runs no GPU work: it reads the
 counter_collection.csv files of two rocprofv3 --pmc runs of this script
