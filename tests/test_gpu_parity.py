@@ -386,6 +386,37 @@ def test_workspace_holds_the_documented_partials(eg, cuda_device, T, H):
     assert rel <= 1e-5
 
 
+def test_row_magnitudes_across_the_supported_range(eg, cuda_device):
+    """Rows of x, of k, or of both scaled by 2^e, from far below eps (where
+    the gate is 1/2) to 2^56, inside the supported range H max|x|^2 < 2^128
+    (fp32 sums of squares, as in an fp32 RMSNorm). Every row of every output
+    is compared with the oracle on its own."""
+    H = 4096
+    exps = (-120, -64, -40, -20, 0, 20, 40, 50, 56)
+    cases = [(e, w) for e in exps for w in ("x", "k", "both")]
+
+    def fill(d):
+        for t, (e, w) in enumerate(cases):
+            for n in ("x", "k"):
+                if w in (n, "both"):
+                    d[n][t] = synth.round_bf16(synth.bf16_to_f64(d[n][t]) * 2.0 ** e)
+    d = make_case(len(cases), H, seed=29, fill=fill)
+    g = run_gpu(eg, d, cuda_device)
+    assert_report(compare(d, g), name="row magnitudes 2^-120 .. 2^56")
+    assert_dv_is_gate_times_grad(d, g)
+    o_dx, o_dk, o_dv, _, _, _ = oracle.bwd_bf16(d["grad_out"], d["x"], d["k"], d["v"],
+                                                d["wh"], d["we"])
+    worst = 0.0
+    for name, o in (("dx", o_dx), ("dk", o_dk), ("dv", o_dv)):
+        ref = oracle.bf16_to_f64(oracle.round_bf16(o))
+        got = oracle.bf16_to_f64(g[name])
+        assert np.all(np.isfinite(got)), name
+        rel = np.linalg.norm(got - ref, axis=1) / np.linalg.norm(ref, axis=1)
+        worst = max(worst, float(rel.max()))
+        assert np.all(rel <= REL_TOL), (name, [cases[i] for i in np.flatnonzero(rel > REL_TOL)])
+    say(f"[row magnitudes] worst row rel L2 {worst:.3e}")
+
+
 def test_empty_and_zero_partials(eg, cuda_device):
     import torch
     dev = cuda_device
