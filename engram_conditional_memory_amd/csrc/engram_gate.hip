@@ -17,22 +17,25 @@
 // of the next rows are already in flight.
 //
 // Algebra used by both passes. With w_i = wh_i * we_i (the product of the
-// two RMSNorm weights),
-//   d = r_x r_k sum_i x_i k_i w_i,  P = sum_i x_i k_i w_i,
+// two RMSNorm weights) and the normalised rows x^ = r_x x, k^ = r_k k,
+//   d = r_x r_k sum_i x_i k_i w_i,
 // and the chain rule through out = x + gate * v gives per row
 //   dd = (sum_i gout_i v_i) * g (1 - g) / (2 sqrt(max(|z|, clamp))) / sqrt(H)
-//   dx_i = gout_i + A w_i k_i - Bx x_i,   dk_i = A w_i x_i - Bk k_i,
+//   dx_i = gout_i + (dd r_x) w_i k^_i - (dd r_x d / H) x^_i,
+//   dk_i =          (dd r_k) w_i x^_i - (dd r_k d / H) k^_i,
 //   dv_i = g gout_i,
-//   A = dd r_x r_k,  Bx = dd r_x^2 d / H,  Bk = dd r_k^2 d / H,
-// and the weight gradients share one column vector c_i = sum_t A_t x_ti k_ti:
+// and the weight gradients share one column vector c_i = sum_t dd_t x^_ti k^_ti:
 //   dL/dwh_i = we_i c_i,   dL/dwe_i = wh_i c_i.
 //
-// Precision: x_i * k_i is exact in fp32 (two 8-bit significands); it is
-// multiplied by w_i and accumulated in fp64, so the dot product that decides
-// the gate near z = 0 carries no cancellation error worth the name. The
-// sums of squares and of gout*v are fp32; the per-row scalars use the
-// hardware's fp32 reciprocal, square root and exp2 (about 1 ulp each), whose
-// relative errors move the gate by < 1e-7.
+// Precision and range: every row sum (of x^2, k^2, x k w and gout v) is
+// accumulated in fp64 from exact fp64 products of the bf16 values, and the
+// row scalars r_x, r_k, d and dd are fp64. The dot product that decides the
+// gate near z = 0 thus carries only relative rounding error, and no finite
+// bf16 row overflows or underflows on its way to the gate: the elementwise
+// work is fp32 on the normalised rows, whose mean squares are at most 1,
+// with coefficients rounded to fp32 only after they are formed in fp64.
+// The gate itself uses the hardware's fp32 square root, exp2 and reciprocal
+// (about 1 ulp each), which move it by < 1e-7.
 
 #include <hip/hip_runtime.h>
 
@@ -207,18 +210,27 @@ __device__ __forceinline__ WeightsLds<NT, C> stage_weights(const double (&w64)[C
 }
 
 struct RowScalars {
-  float r_x, r_k, d, z, g;
+  double r_x, r_k, d;  // 1/sqrt(mean(x^2) + eps), likewise for k, the dot d
+  float z, g;          // z = d / sqrt(H), gate
 };
 
+// 1/sqrt(m) for m >= eps: the hardware estimate and one Newton step.
+__device__ __forceinline__ double rsqrt64(double m) {
+  const double r = __builtin_amdgcn_rsq(m);
+  return r * fma(-0.5 * m * r, r, 1.5);
+}
+
 // Gate of one row from its three sums (formula of the section "5. Engram").
-__device__ __forceinline__ RowScalars row_gate(float sum_xx, float sum_kk,
-                                               double sum_xkw, float eps,
-                                               float inv_h, float inv_sqrt_h) {
+// Everything that scales with the data stays in fp64, so no row of finite
+// bf16 values overflows or underflows on its way to z, which is O(H^(1/2)).
+__device__ __forceinline__ RowScalars row_gate(double sum_xx, double sum_kk,
+                                               double sum_xkw, double eps,
+                                               double inv_h, double inv_sqrt_h) {
   RowScalars s;
-  s.r_x = __builtin_amdgcn_rsqf(fmaf(sum_xx, inv_h, eps));
-  s.r_k = __builtin_amdgcn_rsqf(fmaf(sum_kk, inv_h, eps));
-  s.d = (float)sum_xkw * s.r_x * s.r_k;
-  s.z = s.d * inv_sqrt_h;
+  s.r_x = rsqrt64(fma(sum_xx, inv_h, eps));
+  s.r_k = rsqrt64(fma(sum_kk, inv_h, eps));
+  s.d = sum_xkw * s.r_x * s.r_k;
+  s.z = (float)(s.d * inv_sqrt_h);
   // signed_sqrt: sign(z) sqrt|z|, with sign(0) = 0
   const float sq = copysignf(__builtin_amdgcn_sqrtf(fabsf(s.z)), s.z);
   // sigmoid(sq) = 1 / (1 + 2^(-sq log2 e))
@@ -289,16 +301,14 @@ __device__ __forceinline__ void fwd_load(FwdBuf<C>& b, const u32x4* __restrict__
 template <int W, int C, bool FULL, class WT>
 __device__ __forceinline__ void fwd_row(const FwdBuf<C>& b, int64_t r, int slot,
                                         int tid, int nchunk, const WT& w64,
-                                        float (&red_f)[2][2][W],
-                                        double (&red_d)[2][W],
+                                        double (&red)[2][3][W],
                                         u32x4* __restrict__ out,
-                                        float* __restrict__ gate, float eps,
-                                        float inv_h, float inv_sqrt_h) {
+                                        float* __restrict__ gate, double eps,
+                                        double inv_h, double inv_sqrt_h) {
   constexpr int NT = W * kWave;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
-  float sxx = 0.f, skk = 0.f;
-  double sxkw = 0.0;
+  double sxx = 0.0, skk = 0.0, sxkw = 0.0;
 #pragma unroll
   for (int j = 0; j < C; ++j) {
     float xf[8], kf[8];
@@ -306,28 +316,29 @@ __device__ __forceinline__ void fwd_row(const FwdBuf<C>& b, int64_t r, int slot,
     unpack8(b.k[j], kf);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      sxx = fmaf(xf[e], xf[e], sxx);
-      skk = fmaf(kf[e], kf[e], skk);
-      // x_i k_i is exact in fp32 (two 8-bit significands)
-      sxkw = fma((double)(xf[e] * kf[e]), w64.get(j, e), sxkw);
+      // squares and x_i k_i are exact in fp64 (8-bit significands) at any
+      // bf16 magnitude
+      const double xd = xf[e], kd = kf[e];
+      sxx = fma(xd, xd, sxx);
+      skk = fma(kd, kd, skk);
+      sxkw = fma(xd * kd, w64.get(j, e), sxkw);
     }
   }
   sxx = wave_sum(sxx);
   skk = wave_sum(skk);
   sxkw = wave_sum(sxkw);
   if (lane == 0) {
-    red_f[slot][0][wave] = sxx;
-    red_f[slot][1][wave] = skk;
-    red_d[slot][wave] = sxkw;
+    red[slot][0][wave] = sxx;
+    red[slot][1][wave] = skk;
+    red[slot][2][wave] = sxkw;
   }
   __syncthreads();
-  float txx = 0.f, tkk = 0.f;
-  double txkw = 0.0;
+  double txx = 0.0, tkk = 0.0, txkw = 0.0;
 #pragma unroll
   for (int i = 0; i < W; ++i) {
-    txx += red_f[slot][0][i];
-    tkk += red_f[slot][1][i];
-    txkw += red_d[slot][i];
+    txx += red[slot][0][i];
+    tkk += red[slot][1][i];
+    txkw += red[slot][2][i];
   }
   const RowScalars s = row_gate(txx, tkk, txkw, eps, inv_h, inv_sqrt_h);
 
@@ -352,12 +363,11 @@ __global__ __launch_bounds__(W * kWave) void gate_fwd_kernel(
     const u32x4* __restrict__ x, const u32x4* __restrict__ k,
     const u32x4* __restrict__ v, const f32x4* __restrict__ wh,
     const f32x4* __restrict__ we, u32x4* __restrict__ out,
-    float* __restrict__ gate, RowWalk walk, int nchunk, float eps, float inv_h,
-    float inv_sqrt_h) {
+    float* __restrict__ gate, RowWalk walk, int nchunk, double eps, double inv_h,
+    double inv_sqrt_h) {
   constexpr int NT = W * kWave;
   const int tid = threadIdx.x;
-  __shared__ float red_f[2][2][W];
-  __shared__ double red_d[2][W];
+  __shared__ double red[2][3][W];
 
   const int64_t blk = xcd_slab_block();
   const int64_t first = blk * walk.block_stride;
@@ -378,7 +388,7 @@ __global__ __launch_bounds__(W * kWave) void gate_fwd_kernel(
       fwd_load<NT, C, FULL>(buf[(s + D - 1) % D], x, k, v, row(i + s + D - 1), nchunk,
                             tid);
       fwd_row<W, C, FULL>(buf[s], row(i + s), (int)((i + s) & 1), tid, nchunk, w64,
-                          red_f, red_d, out, gate, eps, inv_h, inv_sqrt_h);
+                          red, out, gate, eps, inv_h, inv_sqrt_h);
       if (i + s + 1 >= n) return;
     }
   }
@@ -408,18 +418,17 @@ template <int W, int C, bool FULL, class WT>
 __device__ __forceinline__ void bwd_row(const BwdBuf<C>& b, int64_t r, int slot,
                                         int tid, int nchunk, const WT& w64,
                                         float (&cacc)[C][8],
-                                        float (&red_f)[2][3][W],
-                                        double (&red_d)[2][W],
+                                        double (&red)[2][4][W],
                                         u32x4* __restrict__ dx,
                                         u32x4* __restrict__ dk,
-                                        u32x4* __restrict__ dv, float eps,
-                                        float clamp, float inv_h,
-                                        float inv_sqrt_h) {
+                                        u32x4* __restrict__ dv, double eps,
+                                        float clamp, double inv_h,
+                                        double inv_sqrt_h) {
   constexpr int NT = W * kWave;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
-  float sxx = 0.f, skk = 0.f, sgv = 0.f;
-  double sxkw = 0.0;
+  // the forward's sums in the forward's order, so the gate has its bits
+  double sxx = 0.0, skk = 0.0, sxkw = 0.0, sgv = 0.0;
 #pragma unroll
   for (int j = 0; j < C; ++j) {
     float gf[8], xf[8], kf[8], vf[8];
@@ -429,10 +438,11 @@ __device__ __forceinline__ void bwd_row(const BwdBuf<C>& b, int64_t r, int slot,
     unpack8(b.k[j], kf);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      sgv = fmaf(gf[e], vf[e], sgv);
-      sxx = fmaf(xf[e], xf[e], sxx);
-      skk = fmaf(kf[e], kf[e], skk);
-      sxkw = fma((double)(xf[e] * kf[e]), w64.get(j, e), sxkw);
+      const double xd = xf[e], kd = kf[e];
+      sgv = fma((double)gf[e], (double)vf[e], sgv);
+      sxx = fma(xd, xd, sxx);
+      skk = fma(kd, kd, skk);
+      sxkw = fma(xd * kd, w64.get(j, e), sxkw);
     }
   }
   sxx = wave_sum(sxx);
@@ -440,31 +450,35 @@ __device__ __forceinline__ void bwd_row(const BwdBuf<C>& b, int64_t r, int slot,
   sgv = wave_sum(sgv);
   sxkw = wave_sum(sxkw);
   if (lane == 0) {
-    red_f[slot][0][wave] = sxx;
-    red_f[slot][1][wave] = skk;
-    red_f[slot][2][wave] = sgv;
-    red_d[slot][wave] = sxkw;
+    red[slot][0][wave] = sxx;
+    red[slot][1][wave] = skk;
+    red[slot][2][wave] = sxkw;
+    red[slot][3][wave] = sgv;
   }
   __syncthreads();
-  float txx = 0.f, tkk = 0.f, tgv = 0.f;
-  double txkw = 0.0;
+  double txx = 0.0, tkk = 0.0, txkw = 0.0, tgv = 0.0;
 #pragma unroll
   for (int i = 0; i < W; ++i) {
-    txx += red_f[slot][0][i];
-    tkk += red_f[slot][1][i];
-    tgv += red_f[slot][2][i];
-    txkw += red_d[slot][i];
+    txx += red[slot][0][i];
+    tkk += red[slot][1][i];
+    txkw += red[slot][2][i];
+    tgv += red[slot][3][i];
   }
   const RowScalars s = row_gate(txx, tkk, txkw, eps, inv_h, inv_sqrt_h);
   // gate = sigmoid(sq): d gate / d sq = g (1 - g);
   // sq = signed_sqrt(z): d sq / dz = 1 / (2 sqrt(max(|z|, clamp)));
   // z = d / sqrt(H).
-  const float ds = tgv * s.g * (1.0f - s.g);
-  const float dz = ds * 0.5f * __builtin_amdgcn_rsqf(fmaxf(fabsf(s.z), clamp));
-  const float dd = dz * inv_sqrt_h;
-  const float A = dd * s.r_x * s.r_k;
-  const float Bx = dd * s.r_x * s.r_x * s.d * inv_h;
-  const float Bk = dd * s.r_k * s.r_k * s.d * inv_h;
+  const float half_dsq = 0.5f * __builtin_amdgcn_rsqf(fmaxf(fabsf(s.z), clamp));
+  const double dd = tgv * (double)(s.g * (1.0f - s.g)) * (double)half_dsq * inv_sqrt_h;
+  // With x^ = r_x x and k^ = r_k k, whose mean squares are at most 1:
+  //   dx = gout + (dd r_x) w k^ - (dd r_x d / H) x^
+  //   dk =        (dd r_k) w x^ - (dd r_k d / H) k^
+  //   c += dd x^ k^
+  // Every coefficient is formed in fp64 before it is rounded to fp32.
+  const float rxf = (float)s.r_x, rkf = (float)s.r_k;
+  const float ax = (float)(dd * s.r_x), bx = (float)(dd * s.r_x * s.d * inv_h);
+  const float ak = (float)(dd * s.r_k), bk = (float)(dd * s.r_k * s.d * inv_h);
+  const float cd = (float)dd;
 
   const int64_t o = r * nchunk;
 #pragma unroll
@@ -478,10 +492,11 @@ __device__ __forceinline__ void bwd_row(const BwdBuf<C>& b, int64_t r, int slot,
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float w = (float)w64.get(j, e);
-        ox[e] = fmaf(-Bx, xf[e], fmaf(A, w * kf[e], gf[e]));
-        ok[e] = fmaf(-Bk, kf[e], A * (w * xf[e]));
+        const float xh = rxf * xf[e], kh = rkf * kf[e];
+        ox[e] = fmaf(-bx, xh, fmaf(ax, w * kh, gf[e]));
+        ok[e] = fmaf(-bk, kh, ak * (w * xh));
         ov[e] = s.g * gf[e];
-        cacc[j][e] = fmaf(A, xf[e] * kf[e], cacc[j][e]);
+        cacc[j][e] = fmaf(cd, xh * kh, cacc[j][e]);
       }
       store_chunk(dx + o + c, pack8(ox));
       store_chunk(dk + o + c, pack8(ok));
@@ -496,12 +511,11 @@ __global__ __launch_bounds__(W * kWave) void gate_bwd_kernel(
     const u32x4* __restrict__ k, const u32x4* __restrict__ v,
     const f32x4* __restrict__ wh, const f32x4* __restrict__ we,
     u32x4* __restrict__ dx, u32x4* __restrict__ dk, u32x4* __restrict__ dv,
-    f32x4* __restrict__ partial, RowWalk walk, int nchunk, float eps,
-    float clamp, float inv_h, float inv_sqrt_h) {
+    f32x4* __restrict__ partial, RowWalk walk, int nchunk, double eps,
+    float clamp, double inv_h, double inv_sqrt_h) {
   constexpr int NT = W * kWave;
   const int tid = threadIdx.x;
-  __shared__ float red_f[2][3][W];
-  __shared__ double red_d[2][W];
+  __shared__ double red[2][4][W];
 
   // c_i over this block's rows, for the thread's columns.
   float cacc[C][8];
@@ -530,7 +544,7 @@ __global__ __launch_bounds__(W * kWave) void gate_bwd_kernel(
           bwd_load<NT, C, FULL>(buf[(s + D - 1) % D], gout, x, k, v,
                                 row(i + s + D - 1), nchunk, tid);
           bwd_row<W, C, FULL>(buf[s], row(i + s), (int)((i + s) & 1), tid, nchunk,
-                              wts, cacc, red_f, red_d, dx, dk, dv, eps, clamp, inv_h,
+                              wts, cacc, red, dx, dk, dv, eps, clamp, inv_h,
                               inv_sqrt_h);
           if (i + s + 1 >= n) return;
         }
@@ -723,7 +737,8 @@ Plan fwd_plan(int nchunk) {
   if (nchunk == 512) return {4, 2, 2, true, false, 256};   // H = 4096
   if (nchunk == 640) return {5, 2, 2, true, false, 256};   // H = 5120
   if (nchunk == 384) return {3, 2, 3, true, false, 256};   // H = 3072
-  if (nchunk == 256) return {2, 2, 2, true, false, 512};   // H = 2048
+  if (nchunk == 256) return {1, 4, 2, true, false, 512};   // H = 2048
+  if (nchunk == 768) return {3, 4, 2, true, false, 256};   // H = 6144
   return generic_plan(nchunk);
 }
 
@@ -732,7 +747,8 @@ Plan bwd_plan(int nchunk) {
   if (nchunk == 512) return {4, 2, 2, true, false, 256};   // H = 4096
   if (nchunk == 640) return {5, 2, 2, true, false, 256};   // H = 5120
   if (nchunk == 384) return {3, 2, 2, true, false, 256};   // H = 3072
-  if (nchunk == 256) return {2, 2, 3, true, false, 256};   // H = 2048
+  if (nchunk == 256) return {1, 4, 2, true, false, 512};   // H = 2048
+  if (nchunk == 768) return {3, 4, 2, true, true, 256};    // H = 6144
   return generic_plan(nchunk);
 }
 
@@ -761,7 +777,7 @@ struct FwdArgs {
   float* gate;
   RowWalk walk;
   int nchunk;
-  float eps, inv_h, inv_sqrt_h;
+  double eps, inv_h, inv_sqrt_h;
 };
 
 template <int W, int C, bool FULL, int D>
@@ -776,7 +792,8 @@ tk_status dispatch_fwd(const Plan& p, const FwdArgs& a, int grid, hipStream_t st
   if (p.W == 4 && p.C == 2 && p.full && p.D == 2) return run_fwd<4, 2, true, 2>(a, grid, st);
   if (p.W == 5 && p.C == 2 && p.full && p.D == 2) return run_fwd<5, 2, true, 2>(a, grid, st);
   if (p.W == 3 && p.C == 2 && p.full && p.D == 3) return run_fwd<3, 2, true, 3>(a, grid, st);
-  if (p.W == 2 && p.C == 2 && p.full && p.D == 2) return run_fwd<2, 2, true, 2>(a, grid, st);
+  if (p.W == 1 && p.C == 4 && p.full && p.D == 2) return run_fwd<1, 4, true, 2>(a, grid, st);
+  if (p.W == 3 && p.C == 4 && p.full && p.D == 2) return run_fwd<3, 4, true, 2>(a, grid, st);
   if (p.D == 2 && p.C == 1) {
     switch (p.W) {
       case 1: return run_fwd<1, 1, false, 2>(a, grid, st);
@@ -797,7 +814,8 @@ struct BwdArgs {
   f32x4* partial;
   RowWalk walk;
   int nchunk;
-  float eps, clamp, inv_h, inv_sqrt_h;
+  double eps, inv_h, inv_sqrt_h;
+  float clamp;
 };
 
 template <int W, int C, bool FULL, int D, bool WLDS>
@@ -818,8 +836,10 @@ tk_status dispatch_bwd(const Plan& p, const BwdArgs& a, int grid, hipStream_t st
     return run_bwd<5, 2, true, 2, false>(a, grid, st);
   if (p.W == 3 && p.C == 2 && p.full && p.D == 2 && !p.wlds)
     return run_bwd<3, 2, true, 2, false>(a, grid, st);
-  if (p.W == 2 && p.C == 2 && p.full && p.D == 3 && !p.wlds)
-    return run_bwd<2, 2, true, 3, false>(a, grid, st);
+  if (p.W == 1 && p.C == 4 && p.full && p.D == 2 && !p.wlds)
+    return run_bwd<1, 4, true, 2, false>(a, grid, st);
+  if (p.W == 3 && p.C == 4 && p.full && p.D == 2 && p.wlds)
+    return run_bwd<3, 4, true, 2, true>(a, grid, st);
   if (p.D == 2 && !p.wlds && p.C == 1) {
     switch (p.W) {
       case 1: return run_bwd<1, 1, false, 2, false>(a, grid, st);
@@ -873,9 +893,9 @@ tk_status tk_engram_gate_fwd(const uint16_t* x, const uint16_t* k,
   const int grid = (int)grid_of(plan, T);
   a.walk = row_walk(T, grid);
   a.nchunk = nchunk;
-  a.eps = (float)eps;
-  a.inv_h = (float)(1.0 / (double)H);
-  a.inv_sqrt_h = (float)(1.0 / std::sqrt((double)H));
+  a.eps = eps;
+  a.inv_h = 1.0 / (double)H;
+  a.inv_sqrt_h = 1.0 / std::sqrt((double)H);
   return dispatch_fwd(plan, a, grid, reinterpret_cast<hipStream_t>(stream));
 }
 
@@ -912,10 +932,10 @@ tk_status tk_engram_gate_bwd(const uint16_t* grad_out, const uint16_t* x,
   const int grid = (int)grid_of(plan, T);
   a.walk = row_walk(T, grid);
   a.nchunk = nchunk;
-  a.eps = (float)eps;
+  a.eps = eps;
   a.clamp = (float)dsqrt_clamp;
-  a.inv_h = (float)(1.0 / (double)H);
-  a.inv_sqrt_h = (float)(1.0 / std::sqrt((double)H));
+  a.inv_h = 1.0 / (double)H;
+  a.inv_sqrt_h = 1.0 / std::sqrt((double)H);
   return dispatch_bwd(plan, a, grid, reinterpret_cast<hipStream_t>(stream));
 }
 

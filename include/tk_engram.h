@@ -27,15 +27,14 @@
  *     on `stream` (a hipStream_t passed as void*, NULL = default stream)
  *     and returns. Outputs are overwritten, never accumulated into.
  *   - Inputs and outputs must not overlap (undefined behaviour otherwise).
- *   - Arithmetic: fp32 elementwise work with fp32 sums, except the weighted
- *     dot product sum_i x_i k_i wh_i we_i, which is accumulated in fp64 so
- *     that the gate stays accurate where the dot product is near zero.
- *     bf16 results are rounded to nearest, ties to even.
- *   - Range: as in an fp32 RMSNorm, the sums of squares are fp32, so results
- *     follow the fp64 definition while every row keeps H * max|x_i|^2 and
- *     H * max|k_i|^2 below 2^128 (|x|, |k| below about 2^64 / sqrt(H), e.g.
- *     2^57 at H = 7168). Beyond that a row's gate degrades to 1/2, or to NaN
- *     once products x_i * k_i overflow. Small rows are exact down to zero.
+ *   - Arithmetic: every row sum (squares, the weighted dot product
+ *     sum_i x_i k_i wh_i we_i, and sum_i grad_out_i v_i) is accumulated in
+ *     fp64 from exact products, and the per-row scalars are fp64; the
+ *     elementwise work is fp32 on the RMS-normalised rows. So the gate stays
+ *     accurate where the dot product is near zero, and no finite bf16 input,
+ *     however large or small, overflows or underflows on the way (only
+ *     outputs beyond the bf16 range are infinite, as their exact values
+ *     would round). bf16 results are rounded to nearest, ties to even.
  *   - Every call is deterministic: the row-to-workgroup assignment depends
  *     only on (T, H), and no atomics are used, so reruns are bit-identical.
  *   - Errors: arguments are checked before any device work; a failed check

@@ -386,23 +386,26 @@ def test_workspace_holds_the_documented_partials(eg, cuda_device, T, H):
     assert rel <= 1e-5
 
 
-def test_row_magnitudes_across_the_supported_range(eg, cuda_device):
-    """Rows of x, of k, or of both scaled by 2^e, from far below eps (where
-    the gate is 1/2) to 2^56, inside the supported range H max|x|^2 < 2^128
-    (fp32 sums of squares, as in an fp32 RMSNorm). Every row of every output
-    is compared with the oracle on its own."""
+def test_row_magnitudes_across_the_bf16_range(eg, cuda_device):
+    """Rows of x, of k, of both, or of v scaled by 2^e, from far below eps
+    (where the gate is 1/2) to 2^125, near the top of the bf16 range. The
+    sums are fp64 and every coefficient is formed from normalised rows, so
+    nothing overflows on the way; every row of every output is compared with
+    the oracle on its own."""
     H = 4096
-    exps = (-120, -64, -40, -20, 0, 20, 40, 50, 56)
-    cases = [(e, w) for e in exps for w in ("x", "k", "both")]
+    exps = (-120, -64, -40, -20, 0, 20, 40, 56, 60, 64, 80, 100, 120, 125)
+    cases = [(e, w) for e in exps for w in ("x", "k", "both", "v")]
 
     def fill(d):
         for t, (e, w) in enumerate(cases):
-            for n in ("x", "k"):
-                if w in (n, "both"):
+            for n in ("x", "k", "v"):
+                if w == n or (w == "both" and n != "v"):
                     d[n][t] = synth.round_bf16(synth.bf16_to_f64(d[n][t]) * 2.0 ** e)
     d = make_case(len(cases), H, seed=29, fill=fill)
+    for n in ("x", "k", "v"):
+        assert np.all(np.isfinite(synth.bf16_to_f64(d[n])))
     g = run_gpu(eg, d, cuda_device)
-    assert_report(compare(d, g), name="row magnitudes 2^-120 .. 2^56")
+    assert_report(compare(d, g), name="row magnitudes 2^-120 .. 2^125")
     assert_dv_is_gate_times_grad(d, g)
     o_dx, o_dk, o_dv, _, _, _ = oracle.bwd_bf16(d["grad_out"], d["x"], d["k"], d["v"],
                                                 d["wh"], d["we"])
