@@ -386,13 +386,14 @@ def test_workspace_holds_the_documented_partials(eg, cuda_device, T, H):
     assert rel <= 1e-5
 
 
-def test_row_magnitudes_across_the_bf16_range(eg, cuda_device):
+@pytest.mark.parametrize("H", [4096, 7168, 2048, 6144])
+def test_row_magnitudes_across_the_bf16_range(eg, cuda_device, H):
     """Rows of x, of k, of both, or of v scaled by 2^e, from far below eps
     (where the gate is 1/2) to 2^125, near the top of the bf16 range. The
     sums are fp64 and every coefficient is formed from normalised rows, so
     nothing overflows on the way; every row of every output is compared with
-    the oracle on its own."""
-    H = 4096
+    the oracle on its own. The widths cover each kind of plan: 4 x 2 and
+    1 x 4 with weights in registers, 7 x 2 and 3 x 4 with weights in LDS."""
     exps = (-120, -64, -40, -20, 0, 20, 40, 56, 60, 64, 80, 100, 120, 125)
     cases = [(e, w) for e in exps for w in ("x", "k", "both", "v")]
 
@@ -401,11 +402,11 @@ def test_row_magnitudes_across_the_bf16_range(eg, cuda_device):
             for n in ("x", "k", "v"):
                 if w == n or (w == "both" and n != "v"):
                     d[n][t] = synth.round_bf16(synth.bf16_to_f64(d[n][t]) * 2.0 ** e)
-    d = make_case(len(cases), H, seed=29, fill=fill)
+    d = make_case(len(cases), H, seed=29 + H, fill=fill)
     for n in ("x", "k", "v"):
         assert np.all(np.isfinite(synth.bf16_to_f64(d[n])))
     g = run_gpu(eg, d, cuda_device)
-    assert_report(compare(d, g), name="row magnitudes 2^-120 .. 2^125")
+    assert_report(compare(d, g), name=f"row magnitudes 2^-120 .. 2^125, H={H}")
     assert_dv_is_gate_times_grad(d, g)
     o_dx, o_dk, o_dv, _, _, _ = oracle.bwd_bf16(d["grad_out"], d["x"], d["k"], d["v"],
                                                 d["wh"], d["we"])
@@ -417,7 +418,7 @@ def test_row_magnitudes_across_the_bf16_range(eg, cuda_device):
         rel = np.linalg.norm(got - ref, axis=1) / np.linalg.norm(ref, axis=1)
         worst = max(worst, float(rel.max()))
         assert np.all(rel <= REL_TOL), (name, [cases[i] for i in np.flatnonzero(rel > REL_TOL)])
-    say(f"[row magnitudes] worst row rel L2 {worst:.3e}")
+    say(f"[row magnitudes H={H}] worst row rel L2 {worst:.3e}")
 
 
 def test_empty_and_zero_partials(eg, cuda_device):
