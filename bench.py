@@ -487,6 +487,10 @@ def main():
     ap.add_argument("--widths", action="store_true",
                     help="instead of the default run, time the forward and backward kernels "
                          "at H = " + ", ".join(map(str, WIDTHS)) + " (one JSON line each)")
+    ap.add_argument("--memory-read", action="store_true",
+                    help="instead of the default run, time only the copy probe (470 MB each "
+                         "way, the counters' calibration) and the table gather on uniform and "
+                         "Zipf(1) token ids (one JSON line); for rocprofv3 counter runs")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="summarise two rocprofv3 --pmc runs instead of benchmarking")
     args = ap.parse_args()
@@ -509,6 +513,14 @@ def main():
     if args.widths:
         for r in time_widths(eg, dev):
             print(json.dumps(r))
+        return
+    if args.memory_read:
+        import synth
+        c = synth.CONFIGS[4]
+        copy = copy_ceiling(2 * c.T * c.H, eg, dev)
+        gather_res, gather_zipf_res = time_gather(eg, dev)
+        print(json.dumps({"copy_probe": copy, "gather": gather_res,
+                          "gather_zipf": gather_zipf_res}))
         return
 
     print(f"[bench] generating workload {args.workload}", file=sys.stderr, flush=True)
