@@ -10,8 +10,9 @@ HIP events on the launch stream against 8 TB/s), the same figures for the
 other tuned width and the stress workload, the 1024-token forward hot and
 after a cache scrub, a 128-bit tiled copy and the read/write-mix probes as
 practical HBM ceilings, the N-gram hash and the table gather (uniform and
-Zipf(1) token ids), the autograd module's step, the fused weight, and the
-fp64 oracle's throughput on the host as a reported CPU baseline.
+Zipf(1) token ids), the autograd module's step, the fused weight, a short
+step eager and replayed from a HIP graph, and the fp64 oracle's throughput
+on the host as a reported CPU baseline.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 4]
 
@@ -240,6 +241,49 @@ def time_widths(eg, dev, reps: int = 30) -> list:
         del x, k, v, go, out, gate, dx, dk, dv, ws
         torch.cuda.empty_cache()
     return res
+
+
+def time_graph_step(eg, dev, T: int = 1024, H: int = 4096, reps: int = 50) -> dict:
+    """One step (forward, backward, reduction) on a short batch, called eagerly
+    through the Python binding and replayed from a captured HIP graph; the
+    three calls allocate nothing and write no memset, so they capture as
+    they are. HIP events over back-to-back steps on the launch stream."""
+    import torch
+    g = torch.Generator(device=dev).manual_seed(T + H)
+
+    def mk():
+        return torch.randn((T, H), device=dev, generator=g).to(torch.bfloat16)
+
+    x, k, v, go = mk(), mk(), mk(), mk()
+    wh = 1 + 0.1 * torch.randn(H, device=dev, generator=g)
+    we = 1 + 0.1 * torch.randn(H, device=dev, generator=g)
+    out, dx, dk, dv = (torch.empty_like(x) for _ in range(4))
+    gate = torch.empty((T,), device=dev)
+    P = eg.tk_engram_num_partials(T, H)
+    ws = torch.empty((P, H), device=dev)
+    dwh, dwe = torch.empty(H, device=dev), torch.empty(H, device=dev)
+
+    def step():
+        eg.tk_engram_gate_fwd(x, k, v, wh, we, out, gate)
+        eg.tk_engram_gate_bwd(go, x, k, v, wh, we, dx, dk, dv, ws)
+        eg.tk_engram_grad_w_reduce(ws, P, H, wh, we, dwh, dwe)
+
+    eager = avg_launch_us(step, reps)
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream(dev).wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    replay = avg_launch_us(graph.replay, reps)
+    del graph, x, k, v, go, out, dx, dk, dv, ws
+    torch.cuda.empty_cache()
+    return {"T": T, "H": H, "eager_us": eager, "graph_us": replay,
+            "eager_over_graph": eager / replay,
+            "graph_tokens_per_s": T / (replay / 1e6)}
 
 
 def time_hash(eg, dev, name: str = "b1024s4096", reps: int = 20) -> dict:
@@ -565,13 +609,16 @@ def main():
     main_res["fwd"]["frac_of_mix_ceiling"] = main_res["fwd"]["GBps"] / ceilings["fwd_3r1w"]["GBps"]
     main_res["bwd_kernel"]["frac_of_mix_ceiling"] = (main_res["bwd_kernel"]["GBps"]
                                                      / ceilings["bwd_4r3w"]["GBps"])
-    hash_res = gather_res = gather_zipf_res = fused_res = None
+    hash_res = gather_res = gather_zipf_res = fused_res = graph_res = None
     if not args.no_secondary:
         print("[bench] timing the N-gram hash", file=sys.stderr, flush=True)
         hash_res = time_hash(eg, dev)
         print("[bench] timing the hashed gather", file=sys.stderr, flush=True)
         gather_res, gather_zipf_res = time_gather(eg, dev)
         fused_res = time_fused_weight(eg, dev, main_res["H"])
+        print("[bench] timing a short step eagerly and from a HIP graph", file=sys.stderr,
+              flush=True)
+        graph_res = time_graph_step(eg, dev)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -612,6 +659,7 @@ def main():
         "gather": gather_res,
         "autograd": autograd_res,
         "fused_weight": fused_res,
+        "graph_step_small": graph_res,
         "gather_zipf": gather_zipf_res,
         "cpu_baseline": cpu,
     }
