@@ -15,7 +15,7 @@ const char* tk_status_string(tk_status s) {
     case TK_ERR_NULL:
       return "a required pointer is NULL";
     case TK_ERR_SHAPE:
-      return "invalid shape: a negative count, a non-positive width, or P inconsistent with T";
+      return "invalid shape: a negative count or a non-positive width or table count";
     case TK_ERR_ALIGN:
       return "a width is not a multiple of 8, or a pointer is not aligned as the call requires";
     case TK_ERR_UNSUPPORTED:

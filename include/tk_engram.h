@@ -22,10 +22,13 @@
  * Conventions shared by every call:
  *   - Tensors are row-major and contiguous. bf16 tensors cross the ABI as
  *     uint16_t bit patterns; [T, H] means row stride H elements.
- *   - All pointers are DEVICE pointers owned by the caller. The library
- *     never allocates, frees or synchronises; each call only enqueues work
- *     on `stream` (a hipStream_t passed as void*, NULL = default stream)
- *     and returns. Outputs are overwritten, never accumulated into.
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the hash,
+ *     the gather and the stream probe also take small HOST arrays (of
+ *     parameters or of device pointers), read before the call returns, as
+ *     stated with each call. The library never
+ *     allocates, frees or synchronises; each call only enqueues work on
+ *     `stream` (a hipStream_t passed as void*, NULL = default stream) and
+ *     returns. Outputs are overwritten, never accumulated into.
  *   - Inputs and outputs must not overlap (undefined behaviour otherwise).
  *   - Arithmetic: every row sum (squares, the weighted dot product
  *     sum_i x_i k_i wh_i we_i, and sum_i grad_out_i v_i) is accumulated in
@@ -41,10 +44,12 @@
  *     returns its status and enqueues nothing. A launch failure returns
  *     TK_ERR_LAUNCH. Faults inside kernels surface at the caller's next
  *     synchronisation, as for any HIP kernel.
- *   - Shape limits: 0 <= T, 8 <= H <= 8192, H a multiple of 8; T = 0 is a
- *     successful no-op for the forward and backward.
- *   - Alignment: every tensor pointer must be 16-byte aligned (128-bit
- *     loads and stores), except `gate` which needs 4 bytes.
+ *   - Shape limits of the gate calls: 0 <= T, 8 <= H <= 8192, H a multiple
+ *     of 8; T = 0 is a successful no-op. The hash and the gather state
+ *     their own limits below.
+ *   - Alignment: every tensor pointer of the gate calls must be 16-byte
+ *     aligned (128-bit loads and stores), except `gate` which needs 4 bytes;
+ *     the other calls state their own alignment.
  */
 #ifndef TK_ENGRAM_H
 #define TK_ENGRAM_H
@@ -61,7 +66,7 @@ typedef int32_t tk_status;
 enum {
   TK_SUCCESS = 0,
   TK_ERR_NULL = 1,        /* a required pointer is NULL                     */
-  TK_ERR_SHAPE = 2,       /* negative count, width <= 0, P inconsistent    */
+  TK_ERR_SHAPE = 2,       /* negative count, width or table count <= 0     */
   TK_ERR_ALIGN = 3,       /* width not a multiple of 8, pointer misaligned */
   TK_ERR_UNSUPPORTED = 4, /* a size above the call's supported maximum      */
   TK_ERR_WORKSPACE = 5,   /* backward workspace smaller than required       */
