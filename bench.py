@@ -428,12 +428,11 @@ def time_fwd_small(eg, dev, reps: int = 50) -> dict:
             "flushed_frac": nbytes / (flushed * 1e3) / HBM_PEAK_GBPS}
 
 
-def cpu_baseline(host: dict, budget_s: float = 10.0) -> dict:
-    """The fp64 oracle, as it stands, on the host cores: forward + backward
-    (incl. dwh/dwe) over the workload's tokens in chunks, repeating passes
-    over the workload until `budget_s` of wall time is spent."""
+def _oracle_rate(host: dict, threads: int, budget_s: float, backward: bool):
+    """Tokens per second of the fp64 oracle over the workload's tokens in
+    chunks of 4096, repeating passes until `budget_s` of wall time is spent:
+    forward alone, or forward + backward (incl. dwh/dwe)."""
     import oracle
-    th = oracle.default_threads()
     T = host["x"].shape[0]
     chunk = 4096
     done = 0
@@ -442,17 +441,50 @@ def cpu_baseline(host: dict, budget_s: float = 10.0) -> dict:
         a = done % T
         sl = slice(a, min(T, a + chunk))
         oracle.fwd_bf16(host["x"][sl], host["k"][sl], host["v"][sl], host["wh"],
-                        host["we"], want_out=True, threads=th)
-        oracle.bwd_bf16(host["grad_out"][sl], host["x"][sl], host["k"][sl],
-                        host["v"][sl], host["wh"], host["we"], threads=th)
+                        host["we"], want_out=True, threads=threads)
+        if backward:
+            oracle.bwd_bf16(host["grad_out"][sl], host["x"][sl], host["k"][sl],
+                            host["v"][sl], host["wh"], host["we"], threads=threads)
         done += sl.stop - sl.start
         if time.perf_counter() - t0 >= budget_s:
             break
-    dt = time.perf_counter() - t0
-    return {"value": done / dt, "unit": "tokens/s", "cores": th, "kind": "oracle",
+    return done, time.perf_counter() - t0
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(host: dict, budget_s: float = 10.0, side_s: float = 3.0) -> dict:
+    """The fp64 oracle, as it stands, on the host cores. `value` is forward +
+    backward on every thread the oracle uses; beside it, the same on one
+    thread and the forward alone on every thread, each over a shorter
+    sample, with their algorithmic bytes per second."""
+    import oracle
+    th = oracle.default_threads()
+    T, H = host["x"].shape
+    ab = {key: b / T for key, b in algorithmic_bytes(T, H).items()}   # per token
+    done, dt = _oracle_rate(host, th, budget_s, True)
+    done1, dt1 = _oracle_rate(host, 1, side_s, True)
+    donef, dtf = _oracle_rate(host, th, side_s, False)
+    rate, rate1, ratef = done / dt, done1 / dt1, donef / dtf
+    return {"value": rate, "unit": "tokens/s", "cores": th, "kind": "oracle",
             "sample": f"{done} tokens ({done / T:.2f} passes over the {T}-token workload, "
-                      f"chunks of {chunk}), fp64 forward + backward incl. dwh/dwe, "
-                      f"{dt:.1f} s wall on {th} threads"}
+                      f"chunks of 4096), fp64 forward + backward incl. dwh/dwe, "
+                      f"{dt:.1f} s wall on {th} threads",
+            "GBps_equiv": rate * (ab["fwd"] + ab["bwd"]) / 1e9,
+            "single_thread": {"value": rate1, "sample": f"{done1} tokens, {dt1:.1f} s",
+                              "GBps_equiv": rate1 * (ab["fwd"] + ab["bwd"]) / 1e9},
+            "fwd_only": {"value": ratef, "cores": th, "sample": f"{donef} tokens, {dtf:.1f} s",
+                         "GBps_equiv": ratef * ab["fwd"] / 1e9},
+            "cpu_model": cpu_model()}
 
 
 def measured_traffic(kernel: str, workload: str):
