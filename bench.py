@@ -673,7 +673,7 @@ def main():
         "dtype": "f32",
         "data": "synthetic (seeded Philox-4x32-10 inputs of the stated recipe)",
         "config": {"workload": main_res["workload"], "tokens": main_res["T"],
-                   "hidden": main_res["H"], "tensor_dtype": "bf16",
+                   "hidden": main_res["H"], "tensor_dtype": "bf16", "row_sums": "f64",
                    "step": "gate_fwd + gate_bwd + grad_w_reduce", "partials": main_res["P"]},
         "roofline": {"bound": "hbm", "kernel": "gate_bwd_kernel",
                      "achieved": bk["GBps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
