@@ -109,8 +109,10 @@ RowBackward backward_row(const double* gout, const double* x, const double* k,
   for (int64_t i = 0; i < H; ++i) dg += gout[i] * v[i];
   r.dgate = dg;
   for (int64_t i = 0; i < H; ++i) dv[i] = f.gate * gout[i];
-  // gate = sigmoid(s): dgate/ds = gate (1 - gate)
-  r.ds = dg * f.gate * (1.0 - f.gate);
+  // gate = sigmoid(s): dgate/ds = gate (1 - gate). 1 - gate is sigmoid(-s),
+  // evaluated as such: as 1 - gate it would keep only the rounding error of
+  // gate where gate is close to 1 (|s| beyond about 15).
+  r.ds = dg * f.gate * (1.0 / (1.0 + std::exp(f.s)));
   // s = sign(z) sqrt|z|: ds/dz = 1 / (2 sqrt|z|), |z| clamped from below
   r.dz = r.ds * 0.5 / std::sqrt(std::max(std::fabs(f.z), clamp));
   // z = d * scalar

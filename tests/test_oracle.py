@@ -277,6 +277,34 @@ def test_backward_special_cases():
     assert np.all(np.isfinite(dwh)) and np.all(dwh == 0)
 
 
+def test_backward_mirror_in_saturation():
+    # sigmoid' is even, and so is 1/(2 sqrt|z|): k -> -k flips d, z and s but
+    # leaves ds, dz and dd unchanged; d is odd in k, so dk is unchanged and
+    # dx - grad_out changes sign. With large weights s reaches about 36,
+    # where the gate lies within 1e-15 of 1 and its derivative must still
+    # keep full relative precision on both sides.
+    H = 256
+    x = rng_rows(6, H, seed=40)
+    n = rng_rows(6, H, seed=41)
+    rho = np.array([1.0, 0.9, 0.6, 0.3, 0.1, 0.02])[:, None]
+    k = rho * x + np.sqrt(1.0 - rho ** 2) * n
+    v = rng_rows(6, H, seed=42)
+    gout = rng_rows(6, H, seed=43)
+    c = np.full(H, 9.0)
+    dx, dk, _, _, _, bst = oracle.bwd_f64(gout, x, k, v, c, c)
+    mdx, mdk, _, _, _, mbst = oracle.bwd_f64(gout, x, -k, v, c, c)
+    s = oracle.fwd_f64(x, k, v, c, c)[2][:, 6]
+    assert s.max() > 34 and s.min() < 8
+    assert np.all(bst[:, 1] != 0)
+    assert np.allclose(mbst[:, 1:], bst[:, 1:], rtol=1e-12, atol=0)
+    # row by row: the saturated rows' gradients are many orders smaller
+    kscale = np.max(np.abs(dk), 1, keepdims=True)
+    assert np.all(kscale > 0)
+    assert np.all(np.abs(mdk - dk) <= 1e-10 * kscale)
+    xscale = np.max(np.abs(dx - gout), 1, keepdims=True)
+    assert np.all(np.abs((mdx - gout) + (dx - gout)) <= 1e-10 * xscale)
+
+
 def test_clamp_bounds_the_derivative():
     # rows with |z| below the clamp use 1/(2 sqrt(clamp)); above, 1/(2 sqrt|z|)
     H = 256

@@ -47,7 +47,13 @@ MUTANTS = [
     ("dv without the gate", "engram_oracle.cpp",
      "dv[i] = f.gate * gout[i];", "dv[i] = gout[i];"),
     ("sigmoid derivative without (1 - gate)", "engram_oracle.cpp",
-     "r.ds = dg * f.gate * (1.0 - f.gate);", "r.ds = dg * f.gate;"),
+     "r.ds = dg * f.gate * (1.0 / (1.0 + std::exp(f.s)));", "r.ds = dg * f.gate;"),
+    ("sigmoid derivative as gate squared", "engram_oracle.cpp",
+     "r.ds = dg * f.gate * (1.0 / (1.0 + std::exp(f.s)));",
+     "r.ds = dg * f.gate * (1.0 / (1.0 + std::exp(-f.s)));"),
+    ("1 - gate formed by subtraction", "engram_oracle.cpp",
+     "r.ds = dg * f.gate * (1.0 / (1.0 + std::exp(f.s)));",
+     "r.ds = dg * f.gate * (1.0 - f.gate);"),
     ("clamp added instead of taken as a floor", "engram_oracle.cpp",
      "std::max(std::fabs(f.z), clamp)", "(std::fabs(f.z) + clamp)"),
     ("derivative clamp dropped", "engram_oracle.cpp",
