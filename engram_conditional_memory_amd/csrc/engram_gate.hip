@@ -35,7 +35,9 @@
 // work is fp32 on the normalised rows, whose mean squares are at most 1,
 // with coefficients rounded to fp32 only after they are formed in fp64.
 // The gate itself uses the hardware's fp32 square root, exp2 and reciprocal
-// (about 1 ulp each), which move it by < 1e-7.
+// (about 1 ulp each), which move it by < 1e-7. The backward takes the
+// sigmoid's derivative g (1 - g) with 1 - g evaluated as sigmoid(-s), so it
+// keeps its relative precision where the gate saturates toward 1.
 
 #include <hip/hip_runtime.h>
 
@@ -211,7 +213,7 @@ __device__ __forceinline__ WeightsLds<NT, C> stage_weights(const double (&w64)[C
 
 struct RowScalars {
   double r_x, r_k, d;  // 1/sqrt(mean(x^2) + eps), likewise for k, the dot d
-  float z, g;          // z = d / sqrt(H), gate
+  float z, g, gm;      // z = d / sqrt(H), gate, 1 - gate
 };
 
 // 1/sqrt(m) for m >= eps: the hardware estimate and one Newton step.
@@ -236,6 +238,10 @@ __device__ __forceinline__ RowScalars row_gate(double sum_xx, double sum_kk,
   // sigmoid(sq) = 1 / (1 + 2^(-sq log2 e))
   const float e = __builtin_amdgcn_exp2f(-sq * 1.4426950408889634f);
   s.g = __builtin_amdgcn_rcpf(1.0f + e);
+  // 1 - gate = sigmoid(-sq), evaluated as such: 1 - g would keep only g's
+  // rounding error once the gate is within a few ulp of 1 (sq beyond about
+  // 10) and be 0 beyond about 17. Only the backward uses it.
+  s.gm = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(sq * 1.4426950408889634f));
   return s;
 }
 
@@ -465,11 +471,11 @@ __device__ __forceinline__ void bwd_row(const BwdBuf<C>& b, int64_t r, int slot,
     tgv += red[slot][3][i];
   }
   const RowScalars s = row_gate(txx, tkk, txkw, eps, inv_h, inv_sqrt_h);
-  // gate = sigmoid(sq): d gate / d sq = g (1 - g);
+  // gate = sigmoid(sq): d gate / d sq = g (1 - g) = g gm;
   // sq = signed_sqrt(z): d sq / dz = 1 / (2 sqrt(max(|z|, clamp)));
   // z = d / sqrt(H).
   const float half_dsq = 0.5f * __builtin_amdgcn_rsqf(fmaxf(fabsf(s.z), clamp));
-  const double dd = tgv * (double)(s.g * (1.0f - s.g)) * (double)half_dsq * inv_sqrt_h;
+  const double dd = tgv * (double)(s.g * s.gm) * (double)half_dsq * inv_sqrt_h;
   // With x^ = r_x x and k^ = r_k k, whose mean squares are at most 1:
   //   dx = gout + (dd r_x) w k^ - (dd r_x d / H) x^
   //   dk =        (dd r_k) w x^ - (dd r_k d / H) k^

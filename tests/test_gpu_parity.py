@@ -16,6 +16,7 @@ Full-size workloads are compared on every element, streaming the oracle over
 chunks of rows.
 """
 
+import math
 import sys
 
 import numpy as np
@@ -419,6 +420,48 @@ def test_row_magnitudes_across_the_bf16_range(eg, cuda_device, H):
         worst = max(worst, float(rel.max()))
         assert np.all(rel <= REL_TOL), (name, [cases[i] for i in np.flatnonzero(rel > REL_TOL)])
     say(f"[row magnitudes H={H}] worst row rel L2 {worst:.3e}")
+
+
+@pytest.mark.parametrize("H", [4096, 7168, 2048, 6144, 520])
+def test_saturated_gates(eg, cuda_device, H):
+    """Gates from 1/2 to within e^-45 of 0 and of 1. The weights are scaled so
+    that a row with k = x reaches s = 45; k = rho x + sqrt(1 - rho^2) n puts
+    the other rows at s of about 45 sqrt|rho|, of either sign. Where the gate
+    saturates, its derivative g (1 - g) is e^-|s| and the whole dk row (and
+    the gate's share of dx) scales with it, so every row is compared with
+    the oracle on its own: g (1 - g) formed from a gate rounded to fp32
+    would be off by up to 100% there."""
+    targets = np.array([0.5, 2, 5, 8, 10, 12, 15, 17, 20, 25, 30, 35, 40, 45.0])
+    rho = np.concatenate([targets, -targets]) ** 2 / 45.0 ** 2 * np.repeat([1, -1], 14)
+    T = rho.size
+    c = math.sqrt(45.0 ** 2 / math.sqrt(H))
+
+    def fill(d):
+        r = np.random.default_rng(H)
+        x = synth.bf16_to_f64(d["x"])
+        n = r.standard_normal((T, H))
+        d["k"] = synth.round_bf16(rho[:, None] * x + np.sqrt(1 - rho[:, None] ** 2) * n)
+        d["wh"] = (c * (1 + 0.05 * r.standard_normal(H))).astype(np.float32)
+        d["we"] = (c * (1 + 0.05 * r.standard_normal(H))).astype(np.float32)
+    d = make_case(T, H, seed=97 + H, fill=fill)
+    _, o_gate, o_z = oracle.fwd_bf16(d["x"], d["k"], d["v"], d["wh"], d["we"], want_out=False)
+    s = np.sign(o_z) * np.sqrt(np.abs(o_z))
+    assert s.max() > 40 and s.min() < -40 and np.sum(np.abs(s) > 17) >= 8
+    g = run_gpu(eg, d, cuda_device)
+    assert_report(compare(d, g), name=f"saturated gates H={H}")
+    assert_dv_is_gate_times_grad(d, g)
+    o_dx, o_dk, o_dv, _, _, _ = oracle.bwd_bf16(d["grad_out"], d["x"], d["k"], d["v"],
+                                                d["wh"], d["we"])
+    worst = 0.0
+    for name, o in (("dx", o_dx), ("dk", o_dk), ("dv", o_dv)):
+        ref = oracle.bf16_to_f64(oracle.round_bf16(o))
+        got = oracle.bf16_to_f64(g[name])
+        assert np.all(np.isfinite(got)), name
+        rel = np.linalg.norm(got - ref, axis=1) / np.linalg.norm(ref, axis=1)
+        worst = max(worst, float(rel.max()))
+        assert np.all(rel <= REL_TOL), (name, s[rel > REL_TOL])
+    say(f"[saturated gates H={H}] |s| up to {np.abs(s).max():.1f}, "
+        f"worst row rel L2 {worst:.3e}")
 
 
 def test_empty_and_zero_partials(eg, cuda_device):
