@@ -43,10 +43,15 @@ import numpy as np  # noqa: E402
 HBM_PEAK_GBPS = 8000.0          # MI355X published HBM3E bandwidth
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SRC = os.path.join(ROOT, "engram_conditional_memory_amd", "csrc", "engram_gate.hip")
+HASH_SRC = os.path.join(ROOT, "engram_conditional_memory_amd", "csrc", "engram_hash.hip")
+# VALU issue: MI355X has 256 CUs of 4 SIMDs at 2.4 GHz; a SIMD issues one
+# VALU instruction of a 64-wide wave every 4 cycles (16 lanes per cycle)
+VALU_WAVE_INSTS_PER_S = 256 * 4 * 2.4e9 / 4
+HASH_WORKLOAD = "hash_b1024s4096"
 
 
-def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
+def kernel_source_hash(path: str = KERNEL_SRC) -> str:
+    with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
@@ -305,9 +310,12 @@ def time_hash(eg, dev, name: str = "b1024s4096", reps: int = 20) -> dict:
     nbytes = n * (4 + 4 * len(c.ngram) * c.tables)
     del tokens, out
     torch.cuda.empty_cache()
-    return {"workload": c.name, "tokens": n, "us": us, "tokens_per_s": n / (us / 1e6),
-            "bytes": nbytes, "GBps": nbytes / (us * 1e3),
-            "frac": nbytes / (us * 1e3) / HBM_PEAK_GBPS}
+    res = {"workload": c.name, "tokens": n, "us": us, "tokens_per_s": n / (us / 1e6),
+           "bytes": nbytes, "GBps": nbytes / (us * 1e3),
+           "frac": nbytes / (us * 1e3) / HBM_PEAK_GBPS}
+    if name == HASH_WORKLOAD[len("hash_"):]:
+        res["roofline"] = hash_valu_roofline(res["tokens_per_s"])
+    return res
 
 
 def time_gather(eg, dev, reps: int = 20) -> tuple:
@@ -549,6 +557,56 @@ def traffic_from_counters(fetch_csv: str, write_csv: str, workload: int) -> dict
     return rec
 
 
+def valu_from_counters(sq_csv: str) -> dict:
+    """Executed instructions per wave of the N-gram hash on the hash_b1024s4096
+    workload (the 4,194,304-thread dispatches) from one rocprofv3 --pmc run
+    with SQ_WAVES, SQ_INSTS_VALU and SQ_INSTS_SALU; written beside the
+    profiles with the hash source's sha256 prefix."""
+    import csv
+    import synth
+    c = synth.HASH_CONFIGS[HASH_WORKLOAD[len("hash_"):]]
+    threads = str(c.B * c.S)
+    per = {}
+    for r in csv.DictReader(open(sq_csv)):
+        if "hash_kernel" not in r["Kernel_Name"] or r["Grid_Size"] != threads:
+            continue
+        d = per.setdefault(r["Dispatch_Id"], {})
+        d[r["Counter_Name"]] = float(r["Counter_Value"])
+    if not per:
+        raise SystemExit(f"no hash dispatch of {threads} threads in {sq_csv}")
+    valu = float(np.mean([d["SQ_INSTS_VALU"] / d["SQ_WAVES"] for d in per.values()]))
+    salu = float(np.mean([d["SQ_INSTS_SALU"] / d["SQ_WAVES"] for d in per.values()]))
+    waves = float(np.mean([d["SQ_WAVES"] for d in per.values()]))
+    rec = {"workload": HASH_WORKLOAD, "tokens": c.B * c.S, "dispatches": len(per),
+           "waves": waves, "tokens_per_wave": c.B * c.S / waves,
+           "valu_insts_per_wave": valu, "salu_insts_per_wave": salu,
+           "hash_source_sha256_16": kernel_source_hash(HASH_SRC)}
+    path = os.path.join(PROFILES, f"valu_{HASH_WORKLOAD}.json")
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1, sort_keys=True)
+        f.write("\n")
+    return rec
+
+
+def hash_valu_roofline(tokens_per_s: float):
+    """The hash's ALU roofline: tokens per second if every SIMD issued one
+    VALU instruction every 4 cycles, from the committed counter record of
+    the current hash source; None if that record is missing or stale."""
+    path = os.path.join(PROFILES, f"valu_{HASH_WORKLOAD}.json")
+    try:
+        rec = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if rec.get("hash_source_sha256_16") != kernel_source_hash(HASH_SRC):
+        return None
+    peak = VALU_WAVE_INSTS_PER_S * rec["tokens_per_wave"] / rec["valu_insts_per_wave"]
+    return {"bound": "alu", "achieved": tokens_per_s, "peak": peak, "unit": "tokens/s",
+            "frac": tokens_per_s / peak,
+            "basis": f"{rec['valu_insts_per_wave']:.0f} VALU instructions per wave of "
+                     f"{rec['tokens_per_wave']:.0f} tokens (rocprofv3 SQ_INSTS_VALU / "
+                     "SQ_WAVES), one per SIMD every 4 cycles, 1024 SIMDs at 2.4 GHz"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -565,11 +623,18 @@ def main():
                          "at H = " + ", ".join(map(str, WIDTHS)) + " (one JSON line each)")
     ap.add_argument("--memory-read", action="store_true",
                     help="instead of the default run, time only the copy probe (470 MB each "
-                         "way, the counters' calibration) and the table gather on uniform and "
-                         "Zipf(1) token ids (one JSON line); for rocprofv3 counter runs")
+                         "way, the counters' calibration), the N-gram hash and the table "
+                         "gather on uniform and Zipf(1) token ids (one JSON line); for "
+                         "rocprofv3 counter runs")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="summarise two rocprofv3 --pmc runs instead of benchmarking")
+    ap.add_argument("--valu-from", metavar="SQ_CSV",
+                    help="summarise a rocprofv3 --pmc run of SQ_WAVES, SQ_INSTS_VALU and "
+                         "SQ_INSTS_SALU over --memory-read (the hash's instruction counts)")
     args = ap.parse_args()
+    if args.valu_from:
+        print(json.dumps(valu_from_counters(args.valu_from), indent=1, sort_keys=True))
+        return
     if args.traffic_from:
         rec = traffic_from_counters(args.traffic_from[0], args.traffic_from[1], args.workload)
         print(json.dumps(rec, indent=1, sort_keys=True))
@@ -594,8 +659,9 @@ def main():
         import synth
         c = synth.CONFIGS[4]
         copy = copy_ceiling(2 * c.T * c.H, eg, dev)
+        hash_res = time_hash(eg, dev)
         gather_res, gather_zipf_res = time_gather(eg, dev)
-        print(json.dumps({"copy_probe": copy, "gather": gather_res,
+        print(json.dumps({"copy_probe": copy, "hash": hash_res, "gather": gather_res,
                           "gather_zipf": gather_zipf_res}))
         return
 

@@ -10,12 +10,19 @@
 // for p < 0. The multipliers a and table sizes M are the caller's.
 //
 // One thread per token. The few multipliers, sizes and precomputed Barrett
-// reciprocals travel by value in the kernel arguments (scalar registers).
-// The N-gram window of a token is re-read by its neighbours' threads, so
-// the token loads hit in cache; the kernel streams 4 bytes in and 4 * L * K
-// bytes out per token. h mod M is computed exactly with a Barrett quotient
-// q = mulhi64(h, floor((2^64 - 1) / M)), which is at most 2 below
+// reciprocals travel by value in the kernel arguments, one contiguous record
+// per table. The N-gram window of a token is re-read by its neighbours'
+// threads, so the token loads hit in cache; the kernel streams 4 bytes in and
+// 4 * L * K bytes out per token. h mod M is computed exactly with a Barrett
+// quotient q = mulhi64(h, floor((2^64 - 1) / M)), which is at most 2 below
 // floor(h / M), followed by two conditional subtractions.
+//
+// Every table runs the same number of products, NMAX (the largest N of any
+// layer), with the multipliers of positions i >= N set to 0 on the host: a
+// product with 0 leaves the XOR unchanged, so the result is the N-gram hash
+// of the table's own layer, and the kernel has no branches on N. Branching on
+// a table's N made each wave wait for that table's parameters from the
+// scalar cache before it could go on, which cost a third of the throughput.
 
 #include <hip/hip_runtime.h>
 
@@ -32,12 +39,16 @@ constexpr int kMaxTables = TK_ENGRAM_HASH_MAX_TABLES;  // L * K
 constexpr int kMaxN = TK_ENGRAM_HASH_MAX_NGRAM;
 constexpr int kHashBlock = 256;
 
+struct TableParams {
+  uint64_t mult[kMaxN];  // multiplier of window position i; 0 for i >= N
+  uint64_t recip;        // floor((2^64 - 1) / M)
+  uint32_t mod;          // M
+  uint32_t unused;
+};
+
 struct HashParams {
-  uint64_t mult[kMaxTables][kMaxN];
-  uint64_t recip[kMaxTables];  // floor((2^64 - 1) / M)
-  uint32_t mod[kMaxTables];    // M
-  int32_t n[kMaxTables];       // N-gram order of the table's layer
-  int32_t tables;              // L * K
+  TableParams t[kMaxTables];
+  int32_t tables;  // L * K
   uint32_t pad;
 };
 
@@ -49,60 +60,82 @@ __device__ __forceinline__ uint32_t mod_exact(uint64_t h, uint64_t recip, uint32
   return (uint32_t)r;
 }
 
-__device__ __forceinline__ uint32_t table_index(const uint32_t (&tok)[kMaxN],
-                                                const HashParams& p, int q) {
+template <int NMAX>
+__device__ __forceinline__ uint32_t table_index(const uint32_t (&tok)[NMAX],
+                                                const TableParams& t) {
   uint64_t h = 0;
 #pragma unroll
-  for (int i = 0; i < kMaxN; ++i)
-    if (i < p.n[q]) h ^= (uint64_t)tok[i] * p.mult[q][i];
-  return mod_exact(h, p.recip[q], p.mod[q]);
+  for (int i = 0; i < NMAX; ++i) h ^= (uint64_t)tok[i] * t.mult[i];
+  return mod_exact(h, t.recip, t.mod);
 }
 
+// tok[i] = token at position s - i of the sequence, `pad` before its start.
+template <int NMAX>
 __device__ __forceinline__ void window(const int32_t* __restrict__ seq, int64_t s,
-                                       uint32_t pad, uint32_t (&tok)[kMaxN]) {
+                                       uint32_t pad, uint32_t (&tok)[NMAX]) {
 #pragma unroll
-  for (int i = 0; i < kMaxN; ++i) tok[i] = s - i >= 0 ? (uint32_t)seq[s - i] : pad;
+  for (int i = 0; i < NMAX; ++i) tok[i] = s - i >= 0 ? (uint32_t)seq[s - i] : pad;
 }
 
 // L * K == LK, a multiple of 4: each token's indices leave in 16-byte stores.
-template <int LK>
+template <int LK, int NMAX>
 __global__ __launch_bounds__(kHashBlock) void hash_kernel_vec(
     const int32_t* __restrict__ tokens, int64_t S, HashParams p,
     u32x4* __restrict__ out) {
   const int64_t s = (int64_t)blockIdx.x * kHashBlock + threadIdx.x;
   if (s >= S) return;
   const int64_t b = blockIdx.y;
-  uint32_t tok[kMaxN];
-  window(tokens + b * S, s, p.pad, tok);
+  uint32_t tok[NMAX];
+  window<NMAX>(tokens + b * S, s, p.pad, tok);
   u32x4* o = out + (b * S + s) * (LK / 4);
 #pragma unroll
   for (int q4 = 0; q4 < LK / 4; ++q4) {
     u32x4 v;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = table_index(tok, p, 4 * q4 + e);
+    for (int e = 0; e < 4; ++e) v[e] = table_index<NMAX>(tok, p.t[4 * q4 + e]);
     o[q4] = v;
   }
 }
 
 // Any L * K: one 4-byte store per index.
+template <int NMAX>
 __global__ __launch_bounds__(kHashBlock) void hash_kernel_any(
     const int32_t* __restrict__ tokens, int64_t S, HashParams p,
     uint32_t* __restrict__ out) {
   const int64_t s = (int64_t)blockIdx.x * kHashBlock + threadIdx.x;
   if (s >= S) return;
   const int64_t b = blockIdx.y;
-  uint32_t tok[kMaxN];
-  window(tokens + b * S, s, p.pad, tok);
+  uint32_t tok[NMAX];
+  window<NMAX>(tokens + b * S, s, p.pad, tok);
   uint32_t* o = out + (b * S + s) * p.tables;
-  for (int q = 0; q < p.tables; ++q) o[q] = table_index(tok, p, q);
+  for (int q = 0; q < p.tables; ++q) o[q] = table_index<NMAX>(tok, p.t[q]);
 }
 
-template <int LK>
+template <int LK, int NMAX>
 hipError_t launch_vec(const int32_t* tokens, int64_t S, const HashParams& p, void* out,
                       dim3 grid, hipStream_t st) {
-  hipLaunchKernelGGL(hash_kernel_vec<LK>, grid, dim3(kHashBlock), 0, st, tokens, S, p,
-                     reinterpret_cast<u32x4*>(out));
+  hipLaunchKernelGGL((hash_kernel_vec<LK, NMAX>), grid, dim3(kHashBlock), 0, st, tokens, S,
+                     p, reinterpret_cast<u32x4*>(out));
   return hipGetLastError();
+}
+
+template <int NMAX>
+hipError_t launch(const int32_t* tokens, int64_t S, const HashParams& p, void* out,
+                  dim3 grid, hipStream_t st) {
+  switch (p.tables) {
+    case 4: return launch_vec<4, NMAX>(tokens, S, p, out, grid, st);
+    case 8: return launch_vec<8, NMAX>(tokens, S, p, out, grid, st);
+    case 12: return launch_vec<12, NMAX>(tokens, S, p, out, grid, st);
+    case 16: return launch_vec<16, NMAX>(tokens, S, p, out, grid, st);
+    case 20: return launch_vec<20, NMAX>(tokens, S, p, out, grid, st);
+    case 24: return launch_vec<24, NMAX>(tokens, S, p, out, grid, st);
+    case 28: return launch_vec<28, NMAX>(tokens, S, p, out, grid, st);
+    case 32: return launch_vec<32, NMAX>(tokens, S, p, out, grid, st);
+    default:
+      hipLaunchKernelGGL(hash_kernel_any<NMAX>, grid, dim3(kHashBlock), 0, st, tokens, S, p,
+                         reinterpret_cast<uint32_t*>(out));
+      return hipGetLastError();
+  }
 }
 
 }  // namespace
@@ -125,30 +158,25 @@ extern "C" tk_status tk_engram_hash(const int32_t* tokens, int64_t B, int64_t S,
   HashParams p = {};
   p.tables = L * K;
   p.pad = pad;
-  for (int l = 0; l < L; ++l)
+  int nmax = 1;
+  for (int l = 0; l < L; ++l) {
+    nmax = ngram[l] > nmax ? ngram[l] : nmax;
     for (int j = 0; j < K; ++j) {
       const int q = l * K + j;
-      for (int i = 0; i < kMaxN; ++i) p.mult[q][i] = mult[(int64_t)q * kMaxN + i];
-      p.mod[q] = table_size[q];
-      p.recip[q] = UINT64_MAX / table_size[q];
-      p.n[q] = ngram[l];
+      for (int i = 0; i < kMaxN; ++i)
+        p.t[q].mult[i] = i < ngram[l] ? mult[(int64_t)q * kMaxN + i] : 0;
+      p.t[q].mod = table_size[q];
+      p.t[q].recip = UINT64_MAX / table_size[q];
     }
+  }
   const dim3 grid((unsigned)((S + kHashBlock - 1) / kHashBlock), (unsigned)B);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   hipError_t e;
-  switch (p.tables) {
-    case 4: e = launch_vec<4>(tokens, S, p, out, grid, st); break;
-    case 8: e = launch_vec<8>(tokens, S, p, out, grid, st); break;
-    case 12: e = launch_vec<12>(tokens, S, p, out, grid, st); break;
-    case 16: e = launch_vec<16>(tokens, S, p, out, grid, st); break;
-    case 20: e = launch_vec<20>(tokens, S, p, out, grid, st); break;
-    case 24: e = launch_vec<24>(tokens, S, p, out, grid, st); break;
-    case 28: e = launch_vec<28>(tokens, S, p, out, grid, st); break;
-    case 32: e = launch_vec<32>(tokens, S, p, out, grid, st); break;
-    default:
-      hipLaunchKernelGGL(hash_kernel_any, grid, dim3(kHashBlock), 0, st, tokens, S, p,
-                         reinterpret_cast<uint32_t*>(out));
-      e = hipGetLastError();
+  switch (nmax) {
+    case 1: e = launch<1>(tokens, S, p, out, grid, st); break;
+    case 2: e = launch<2>(tokens, S, p, out, grid, st); break;
+    case 3: e = launch<3>(tokens, S, p, out, grid, st); break;
+    default: e = launch<4>(tokens, S, p, out, grid, st); break;
   }
   return e == hipSuccess ? TK_SUCCESS : TK_ERR_LAUNCH;
 }

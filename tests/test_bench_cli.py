@@ -1,5 +1,6 @@
-"""bench.py without a GPU: the multi-GPU refusal, and the rocprofv3 counter
-summary that turns FETCH_SIZE / WRITE_SIZE into bytes per launch."""
+"""bench.py without a GPU: the multi-GPU refusal, the rocprofv3 counter
+summary that turns FETCH_SIZE / WRITE_SIZE into bytes per launch, and the one
+that turns the hash's SQ instruction counts into its ALU roofline."""
 
 import csv
 import json
@@ -60,3 +61,33 @@ def test_traffic_summary_calibrates_on_the_copy_probe(tmp_path, monkeypatch):
     saved["kernel_source_sha256_16"] = "0" * 16
     json.dump(saved, open(tmp_path / f"traffic_{c.name}.json", "w"))
     assert bench.measured_traffic("gate_bwd_kernel", c.name) is None
+
+
+def test_hash_valu_summary_and_alu_roofline(tmp_path, monkeypatch):
+    # two dispatches of the 4,194,304-token hash and one small one (ignored)
+    fields = ["Dispatch_Id", "Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value"]
+    name = "void (anonymous namespace)::hash_kernel_vec<16, 3>(int const*, long)"
+    rows = []
+    for disp, grid, valu in ((1, 4194304, 588), (2, 4194304, 590), (3, 32768, 999)):
+        waves = grid // 64
+        rows += [(disp, grid, "SQ_WAVES", waves), (disp, grid, "SQ_INSTS_VALU", valu * waves),
+                 (disp, grid, "SQ_INSTS_SALU", 18 * waves)]
+    with open(tmp_path / "sq.csv", "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=fields)
+        w.writeheader()
+        for disp, grid, counter, value in rows:
+            w.writerow({"Dispatch_Id": disp, "Kernel_Name": name, "Grid_Size": grid,
+                        "Counter_Name": counter, "Counter_Value": value})
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    rec = bench.valu_from_counters(str(tmp_path / "sq.csv"))
+    assert rec["dispatches"] == 2 and rec["tokens_per_wave"] == 64
+    assert rec["valu_insts_per_wave"] == 589 and rec["salu_insts_per_wave"] == 18
+    # 1024 SIMDs issue one VALU instruction every 4 cycles at 2.4 GHz
+    roof = bench.hash_valu_roofline(30e9)
+    want_peak = 1024 * 2.4e9 / 4 * 64 / 589
+    assert roof["bound"] == "alu" and abs(roof["peak"] - want_peak) < 1
+    assert abs(roof["frac"] - 30e9 / want_peak) < 1e-12
+    saved = json.load(open(tmp_path / "valu_hash_b1024s4096.json"))
+    saved["hash_source_sha256_16"] = "0" * 16
+    json.dump(saved, open(tmp_path / "valu_hash_b1024s4096.json", "w"))
+    assert bench.hash_valu_roofline(30e9) is None

@@ -41,6 +41,9 @@ def test_hash_workloads(eg, cuda_device, name):
     (3, 257, 3, 3, (1, 2, 4)),    # 9 tables: 4-byte stores
     (2, 300, 4, 8, (4, 3, 2, 1)), # 32 tables
     (7, 33, 1, 4, (4,)),
+    (2, 300, 2, 2, (1, 1)),       # N = 1 everywhere, 16-byte stores
+    (4, 513, 1, 5, (3,)),         # 5 tables: 4-byte stores, N = 3
+    (3, 129, 3, 4, (2, 1, 2)),    # 12 tables, largest N = 2
 ])
 def test_hash_shapes_and_orders(eg, cuda_device, B, S, L, K, ngram):
     r = np.random.default_rng(B * 1000 + S)
