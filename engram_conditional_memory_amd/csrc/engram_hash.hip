@@ -14,8 +14,8 @@
 // per table. The N-gram window of a token is re-read by its neighbours'
 // threads, so the token loads hit in cache; the kernel streams 4 bytes in and
 // 4 * L * K bytes out per token. h mod M is computed exactly with a Barrett
-// quotient q = mulhi64(h, floor((2^64 - 1) / M)), which is at most 2 below
-// floor(h / M), followed by two conditional subtractions.
+// quotient q = mulhi64(h, floor((2^64 - 1) / M)), which is at most 1 below
+// floor(h / M), followed by one conditional subtraction in 32 bits.
 //
 // Every table runs the same number of products, NMAX (the largest N of any
 // layer), with the multipliers of positions i >= N set to 0 on the host: a
@@ -38,6 +38,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kMaxTables = TK_ENGRAM_HASH_MAX_TABLES;  // L * K
 constexpr int kMaxN = TK_ENGRAM_HASH_MAX_NGRAM;
 constexpr int kHashBlock = 256;
+constexpr int kWave = 64;
+static_assert(kHashBlock % kWave == 0, "a block holds whole waves");
 
 struct TableParams {
   uint64_t mult[kMaxN];  // multiplier of window position i; 0 for i >= N
@@ -52,12 +54,27 @@ struct HashParams {
   uint32_t pad;
 };
 
+// h mod m for 1 <= m <= 2^31, with R = floor((2^64 - 1) / m).
+//
+// The quotient q = floor(h R / 2^64) is at most one below floor(h / m):
+// R > 2^64 / m - 1 when m is not a power of two (R = floor(2^64 / m) then),
+// and R = 2^64 / m - 1 when it is, so in both cases
+// h R / 2^64 > h / m - h / 2^64 > h / m - 1. Hence r = h - q m lies in
+// [0, 2m), below 2^32, and one conditional subtraction finishes it.
+//
+// Since r < 2^32, only the low 32 bits of q and of q m matter. With
+// h = h1 2^32 + h0 and R = R1 2^32 + R0,
+//   q = h1 R1 + floor(A / 2^32),   A = h1 R0 + h0 R1 + floor(h0 R0 / 2^32),
+// and the bits of A above 64 only reach bits of q above 31, so A is summed
+// modulo 2^64. The subtraction uses min(r, r - m): below m, r - m wraps
+// above r.
 __device__ __forceinline__ uint32_t mod_exact(uint64_t h, uint64_t recip, uint32_t m) {
-  const uint64_t q = __umul64hi(h, recip);
-  uint64_t r = h - q * (uint64_t)m;
-  r = r >= m ? r - m : r;
-  r = r >= m ? r - m : r;
-  return (uint32_t)r;
+  const uint32_t h0 = (uint32_t)h, h1 = (uint32_t)(h >> 32);
+  const uint32_t r0 = (uint32_t)recip, r1 = (uint32_t)(recip >> 32);
+  const uint64_t a = (uint64_t)h1 * r0 + __umulhi(h0, r0) + (uint64_t)h0 * r1;
+  const uint32_t q = h1 * r1 + (uint32_t)(a >> 32);
+  const uint32_t r = h0 - q * m;
+  return min(r, r - m);
 }
 
 template <int NMAX>
@@ -69,46 +86,80 @@ __device__ __forceinline__ uint32_t table_index(const uint32_t (&tok)[NMAX],
   return mod_exact(h, t.recip, t.mod);
 }
 
-// tok[i] = token at position s - i of the sequence, `pad` before its start.
+// tok[i] = token at position s - i of the sequence, `pad` before its start
+// (and for positions s >= S, whose indices are never stored).
 template <int NMAX>
-__device__ __forceinline__ void window(const int32_t* __restrict__ seq, int64_t s,
+__device__ __forceinline__ void window(const int32_t* __restrict__ seq, int64_t s, int64_t S,
                                        uint32_t pad, uint32_t (&tok)[NMAX]) {
 #pragma unroll
-  for (int i = 0; i < NMAX; ++i) tok[i] = s - i >= 0 ? (uint32_t)seq[s - i] : pad;
+  for (int i = 0; i < NMAX; ++i) tok[i] = (s < S && s - i >= 0) ? (uint32_t)seq[s - i] : pad;
 }
 
-// L * K == LK, a multiple of 4: each token's indices leave in 16-byte stores.
+// The 64 tokens of a wave own one contiguous stretch of the output, 64 * LK
+// indices. Each lane hashes its token into the wave's slice of LDS, and the
+// wave then writes the stretch with consecutive lanes on consecutive
+// 16-byte (or 4-byte) words, so every store instruction covers one
+// contiguous span. Written straight from the registers, lane l's indices
+// would sit LK * 4 bytes apart, and each store instruction would touch 64
+// separate pieces of cache lines: that form took 1.6 times as long.
+// Only the wave's own lanes touch its slice, so a wave-level fence orders
+// the LDS writes before the reads.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// L * K == LK, a multiple of 4: the output leaves in 16-byte stores.
 template <int LK, int NMAX>
 __global__ __launch_bounds__(kHashBlock) void hash_kernel_vec(
     const int32_t* __restrict__ tokens, int64_t S, HashParams p,
     u32x4* __restrict__ out) {
-  const int64_t s = (int64_t)blockIdx.x * kHashBlock + threadIdx.x;
-  if (s >= S) return;
+  constexpr int Q4 = LK / 4;  // 16-byte words per token
+  __shared__ u32x4 stage[kHashBlock * Q4];
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int64_t s0 = (int64_t)blockIdx.x * kHashBlock + wave * kWave;  // wave's first token
+  if (s0 >= S) return;
   const int64_t b = blockIdx.y;
   uint32_t tok[NMAX];
-  window<NMAX>(tokens + b * S, s, p.pad, tok);
-  u32x4* o = out + (b * S + s) * (LK / 4);
+  window<NMAX>(tokens + b * S, s0 + lane, S, p.pad, tok);
+  u32x4* ws = stage + wave * kWave * Q4;
 #pragma unroll
-  for (int q4 = 0; q4 < LK / 4; ++q4) {
+  for (int q4 = 0; q4 < Q4; ++q4) {
     u32x4 v;
 #pragma unroll
     for (int e = 0; e < 4; ++e) v[e] = table_index<NMAX>(tok, p.t[4 * q4 + e]);
-    o[q4] = v;
+    ws[lane * Q4 + q4] = v;
+  }
+  wave_lds_sync();
+  const int64_t ntok = S - s0 < kWave ? S - s0 : kWave;  // tokens of this wave
+  u32x4* o = out + (b * S + s0) * Q4;
+#pragma unroll
+  for (int j = 0; j < Q4; ++j) {
+    const int c = j * kWave + lane;
+    if (c < ntok * Q4) o[c] = ws[c];
   }
 }
 
-// Any L * K: one 4-byte store per index.
+// Any L * K (at most kMaxTables): the output leaves in 4-byte stores.
 template <int NMAX>
 __global__ __launch_bounds__(kHashBlock) void hash_kernel_any(
     const int32_t* __restrict__ tokens, int64_t S, HashParams p,
     uint32_t* __restrict__ out) {
-  const int64_t s = (int64_t)blockIdx.x * kHashBlock + threadIdx.x;
-  if (s >= S) return;
+  __shared__ uint32_t stage[kHashBlock * kMaxTables];
+  const int LK = p.tables;
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int64_t s0 = (int64_t)blockIdx.x * kHashBlock + wave * kWave;
+  if (s0 >= S) return;
   const int64_t b = blockIdx.y;
   uint32_t tok[NMAX];
-  window<NMAX>(tokens + b * S, s, p.pad, tok);
-  uint32_t* o = out + (b * S + s) * p.tables;
-  for (int q = 0; q < p.tables; ++q) o[q] = table_index<NMAX>(tok, p.t[q]);
+  window<NMAX>(tokens + b * S, s0 + lane, S, p.pad, tok);
+  uint32_t* ws = stage + wave * kWave * kMaxTables;
+  for (int q = 0; q < LK; ++q) ws[lane * LK + q] = table_index<NMAX>(tok, p.t[q]);
+  wave_lds_sync();
+  const int64_t ntok = S - s0 < kWave ? S - s0 : kWave;
+  uint32_t* o = out + (b * S + s0) * LK;
+  for (int c = lane; c < ntok * LK; c += kWave) o[c] = ws[c];
 }
 
 template <int LK, int NMAX>

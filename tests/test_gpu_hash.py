@@ -1,6 +1,8 @@
 """GPU parity of the N-gram hash (tk_engram_hash through the C ABI) against
 the integer oracle: bit-exact on every index."""
 
+import random
+
 import numpy as np
 import pytest
 
@@ -68,3 +70,47 @@ def test_hash_empty(eg, cuda_device):
     t = torch.empty((0, 5), dtype=torch.int32, device=cuda_device)
     out = eg.tk_engram_hash(t, p["ngram"], p["mult"], p["table_size"], p["pad"])
     assert out.shape == (0, 5, 2, 8)
+
+
+def test_hash_modulus_at_its_edges(eg, cuda_device):
+    """The reduction h mod M at hashes chosen next to multiples of M, at the
+    top of the 64-bit range, and at table sizes 1, 2, powers of two, 2^31 - 1
+    and 2^31. With N = 1 the hash of table q at position 0 is tok * mult[q]
+    mod 2^64; an odd token is invertible modulo 2^64, so mult[q] =
+    target * tok^-1 puts that hash at any chosen target."""
+    r = np.random.default_rng(2024)
+    big = random.Random(2024)          # for integers beyond 64-bit numpy ranges
+    M64 = (1 << 64) - 1
+    sizes_all = [1, 2, 3, 7, 1 << 16, 524287, 524288, (1 << 30) + 1, (1 << 31) - 1, 1 << 31]
+    sizes_all += [int(x) for x in r.integers(1, 1 << 31, size=22)]
+    checked = 0
+    for call in range(24):
+        K = 32
+        sizes = np.array([sizes_all[(call + q) % len(sizes_all)] for q in range(K)],
+                         dtype=np.uint64)
+        tok0 = int(r.integers(0, 1 << 31)) * 2 + 1          # odd, as an unsigned 32-bit id
+        inv = pow(tok0, -1, 1 << 64)
+        targets = []
+        for q in range(K):
+            M = int(sizes[q])
+            top = M64 // M
+            k = big.randrange(max(top - 3, 0), top + 1) if call % 3 == 0 else \
+                big.randrange(0, top + 1)
+            cand = [M64, M64 - 1, k * M, k * M - 1, k * M + M - 1, 0, M - 1]
+            targets.append(cand[(call + q) % len(cand)] % (1 << 64))
+        mult = np.zeros((1, K, 4), dtype=np.uint64)
+        for q in range(K):
+            mult[0, q, 0] = np.uint64((targets[q] * inv) % (1 << 64))
+        S = 5
+        tokens = r.integers(0, 1 << 32, size=(1, S), dtype=np.int64)
+        tokens[0, 0] = tok0
+        tokens = tokens.astype(np.uint32).view(np.int32)
+        want = oracle.engram_hash(tokens, (1,), mult, sizes.astype(np.uint32).reshape(1, K), 0)
+        got = gpu_hash(eg, cuda_device, tokens, (1,), mult,
+                       sizes.astype(np.uint32).reshape(1, K), 0)
+        assert np.array_equal(got, want), call
+        # position 0 hashes to the targets; check those against Python integers
+        row = got.reshape(S, K)[0].astype(np.int64)
+        assert [int(v) for v in row] == [t % int(M) for t, M in zip(targets, sizes)], call
+        checked += K
+    assert checked == 24 * 32
