@@ -48,6 +48,8 @@ HASH_SRC = os.path.join(ROOT, "engram_conditional_memory_amd", "csrc", "engram_h
 # VALU instruction of a 64-wide wave every 4 cycles (16 lanes per cycle)
 VALU_WAVE_INSTS_PER_S = 256 * 4 * 2.4e9 / 4
 HASH_WORKLOAD = "hash_b1024s4096"
+GATHER_SRC = os.path.join(ROOT, "engram_conditional_memory_amd", "csrc", "engram_gather.hip")
+MEMORY_READ_TRAFFIC = "traffic_memory_read.json"
 
 
 def kernel_source_hash(path: str = KERNEL_SRC) -> str:
@@ -351,11 +353,16 @@ def time_gather(eg, dev, reps: int = 20) -> tuple:
         distinct = sum(len(np.unique(ih[:, q])) for q in range(gc.tables))
         n = gc.T * gc.tables
         nbytes = n * (4 + 4 * gc.d)
+        gbps = nbytes / (us * 1e3)
         res.append({"workload": gc.name + ("_zipf" if hc.zipf else ""), "tokens": gc.T,
                     "token_ids": "Zipf(1)" if hc.zipf else "uniform",
                     "rows_gathered": n, "distinct_rows_frac": distinct / n, "us": us,
                     "tokens_per_s": gc.T / (us / 1e6), "bytes": nbytes,
-                    "GBps": nbytes / (us * 1e3), "frac": nbytes / (us * 1e3) / HBM_PEAK_GBPS})
+                    "GBps": gbps, "frac": gbps / HBM_PEAK_GBPS,
+                    "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS,
+                                 "unit": "GB/s", "frac": gbps / HBM_PEAK_GBPS,
+                                 "traffic": memory_read_bytes(
+                                     "gather_zipf" if hc.zipf else "gather")}})
         del tokens, idx, idx2
     del data, out
     torch.cuda.empty_cache()
@@ -588,6 +595,77 @@ def valu_from_counters(sq_csv: str) -> dict:
     return rec
 
 
+def _per_dispatch(path: str, counter: str) -> list:
+    """(dispatch id, kernel base name, grid size, value) of `counter`, in
+    dispatch order."""
+    import csv
+    rows = []
+    for r in csv.DictReader(open(path)):
+        if r.get("Counter_Name") != counter:
+            continue
+        name = r["Kernel_Name"].replace("(anonymous namespace)::", "")
+        if name.startswith("void "):
+            name = name[len("void "):]
+        base = name.split("(")[0].split("<")[0].split("::")[-1].strip()
+        rows.append((int(r["Dispatch_Id"]), base, int(r["Grid_Size"]), float(r["Counter_Value"])))
+    rows.sort()
+    return rows
+
+
+def memory_read_traffic(fetch_csv: str, write_csv: str) -> dict:
+    """HBM bytes per launch of the hash (its 4,194,304-token launches) and of
+    the gather (the first 21 launches on uniform token ids, the next 21 on
+    Zipf(1) ids) from two rocprofv3 --pmc runs over --memory-read, each
+    counter scaled by its reading for the copy probe of known size; written
+    beside the profiles with the two kernel sources' sha256 prefixes."""
+    import synth
+    c4 = synth.CONFIGS[4]
+    copy_bytes = 2 * c4.T * c4.H
+    hc = synth.HASH_CONFIGS[HASH_WORKLOAD[len("hash_"):]]
+    gc = synth.GATHER_CONFIGS["t32768_d448"]
+    rec = {"calibration": {"copy_bytes_each_way": copy_bytes},
+           "hash_source_sha256_16": kernel_source_hash(HASH_SRC),
+           "gather_source_sha256_16": kernel_source_hash(GATHER_SRC)}
+    per = {}
+    for key, path, counter in (("read", fetch_csv, "FETCH_SIZE"), ("write", write_csv, "WRITE_SIZE")):
+        rows = _per_dispatch(path, counter)
+        cp = [v for _, k, _, v in rows if k == "copy_probe_kernel"]
+        scale = copy_bytes / (1024.0 * float(np.mean(cp)))
+        rec["calibration"][f"{counter.lower()}_scale"] = scale
+        hash_v = [v for _, k, g, v in rows if k == "hash_kernel_vec" and g == hc.B * hc.S]
+        gat_v = [v for _, k, _, v in rows if k == "gather_kernel"]
+        if len(gat_v) != 42 or not hash_v:
+            raise SystemExit(f"{path}: expected 42 gather launches and the hash's, "
+                             f"found {len(gat_v)} and {len(hash_v)}")
+        for name, vals in (("hash", hash_v), ("gather", gat_v[:21]), ("gather_zipf", gat_v[21:])):
+            per.setdefault(name, {})[key] = float(np.mean(vals)) * 1024.0 * scale
+    algo = {"hash": hc.B * hc.S * (4 + 4 * len(hc.ngram) * hc.tables),
+            "gather": gc.T * gc.tables * (4 + 4 * gc.d)}
+    algo["gather_zipf"] = algo["gather"]
+    for name, d in per.items():
+        total = d["read"] + d["write"]
+        rec[name] = {"read_bytes": d["read"], "write_bytes": d["write"], "bytes_per_launch": total,
+                     "algorithmic_bytes": algo[name], "measured_over_algorithmic": total / algo[name]}
+    with open(os.path.join(PROFILES, MEMORY_READ_TRAFFIC), "w") as f:
+        json.dump(rec, f, indent=1, sort_keys=True)
+        f.write("\n")
+    return rec
+
+
+def memory_read_bytes(name: str):
+    """Counter bytes per launch of `name` ("hash", "gather", "gather_zipf") from
+    the committed record, if it was taken on the current kernel source."""
+    try:
+        rec = json.load(open(os.path.join(PROFILES, MEMORY_READ_TRAFFIC)))
+    except (OSError, ValueError):
+        return None
+    src = HASH_SRC if name == "hash" else GATHER_SRC
+    key = "hash_source_sha256_16" if name == "hash" else "gather_source_sha256_16"
+    if rec.get(key) != kernel_source_hash(src) or name not in rec:
+        return None
+    return rec[name]["bytes_per_launch"]
+
+
 def hash_valu_roofline(tokens_per_s: float):
     """The hash's ALU roofline: tokens per second if every SIMD issued one
     VALU instruction every 4 cycles, from the committed counter record of
@@ -601,7 +679,7 @@ def hash_valu_roofline(tokens_per_s: float):
         return None
     peak = VALU_WAVE_INSTS_PER_S * rec["tokens_per_wave"] / rec["valu_insts_per_wave"]
     return {"bound": "alu", "achieved": tokens_per_s, "peak": peak, "unit": "tokens/s",
-            "frac": tokens_per_s / peak,
+            "frac": tokens_per_s / peak, "traffic": memory_read_bytes("hash"),
             "basis": f"{rec['valu_insts_per_wave']:.0f} VALU instructions per wave of "
                      f"{rec['tokens_per_wave']:.0f} tokens (rocprofv3 SQ_INSTS_VALU / "
                      "SQ_WAVES), one per SIMD every 4 cycles, 1024 SIMDs at 2.4 GHz"}
@@ -628,10 +706,17 @@ def main():
                          "rocprofv3 counter runs")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="summarise two rocprofv3 --pmc runs instead of benchmarking")
+    ap.add_argument("--memory-read-traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="summarise two rocprofv3 --pmc runs over --memory-read (the hash's "
+                         "and the gather's HBM bytes per launch)")
     ap.add_argument("--valu-from", metavar="SQ_CSV",
                     help="summarise a rocprofv3 --pmc run of SQ_WAVES, SQ_INSTS_VALU and "
                          "SQ_INSTS_SALU over --memory-read (the hash's instruction counts)")
     args = ap.parse_args()
+    if args.memory_read_traffic_from:
+        rec = memory_read_traffic(*args.memory_read_traffic_from)
+        print(json.dumps(rec, indent=1, sort_keys=True))
+        return
     if args.valu_from:
         print(json.dumps(valu_from_counters(args.valu_from), indent=1, sort_keys=True))
         return

@@ -1,6 +1,7 @@
 """bench.py without a GPU: the multi-GPU refusal, the rocprofv3 counter
-summary that turns FETCH_SIZE / WRITE_SIZE into bytes per launch, and the one
-that turns the hash's SQ instruction counts into its ALU roofline."""
+summaries that turn FETCH_SIZE / WRITE_SIZE into bytes per launch (for the
+gate and for the memory read), and the one that turns the hash's SQ
+instruction counts into its ALU roofline."""
 
 import csv
 import json
@@ -91,3 +92,41 @@ def test_hash_valu_summary_and_alu_roofline(tmp_path, monkeypatch):
     saved["hash_source_sha256_16"] = "0" * 16
     json.dump(saved, open(tmp_path / "valu_hash_b1024s4096.json", "w"))
     assert bench.hash_valu_roofline(30e9) is None
+
+
+def test_memory_read_traffic_splits_hash_and_gather(tmp_path, monkeypatch):
+    import synth
+    c = synth.CONFIGS[4]
+    copy_bytes = 2 * c.T * c.H
+    gc = synth.GATHER_CONFIGS["t32768_d448"]
+    g_algo = gc.T * gc.tables * (4 + 4 * gc.d)
+    h_tok = 1024 * 4096
+    fields = ["Dispatch_Id", "Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value"]
+    cp = "(anonymous namespace)::copy_probe_kernel(unsigned int __vector(4) const*, long)"
+    hk = "void (anonymous namespace)::hash_kernel_vec<16, 3>(int const*, long)"
+    gk = "(anonymous namespace)::gather_kernel(int const*, unsigned int __vector(4) const*)"
+    for counter, scale in (("FETCH_SIZE", 2.0), ("WRITE_SIZE", 1.0)):
+        rows = [(cp, 4194304, copy_bytes / scale / 1024)]
+        rows += [(hk, h_tok, (4 * h_tok if counter == "FETCH_SIZE" else 64 * h_tok) / scale / 1024)] * 3
+        rows += [(hk, 32768, 1.0)]            # the gather's own small hash: ignored
+        half = g_algo / 2
+        rows += [(gk, 8388608, half / scale / 1024)] * 21
+        rows += [(gk, 8388608, 0.9 * half / scale / 1024)] * 21
+        with open(tmp_path / f"{counter}.csv", "w", newline="") as f:
+            w = csv.DictWriter(f, fieldnames=fields)
+            w.writeheader()
+            for i, (name, grid, value) in enumerate(rows):
+                w.writerow({"Dispatch_Id": i, "Kernel_Name": name, "Grid_Size": grid,
+                            "Counter_Name": counter, "Counter_Value": value})
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    rec = bench.memory_read_traffic(str(tmp_path / "FETCH_SIZE.csv"),
+                                    str(tmp_path / "WRITE_SIZE.csv"))
+    assert abs(rec["hash"]["measured_over_algorithmic"] - 1.0) < 1e-12
+    assert abs(rec["gather"]["measured_over_algorithmic"] - 1.0) < 1e-12
+    assert abs(rec["gather_zipf"]["measured_over_algorithmic"] - 0.9) < 1e-12
+    assert bench.memory_read_bytes("gather") == rec["gather"]["bytes_per_launch"]
+    saved = json.load(open(tmp_path / bench.MEMORY_READ_TRAFFIC))
+    saved["gather_source_sha256_16"] = "0" * 16
+    json.dump(saved, open(tmp_path / bench.MEMORY_READ_TRAFFIC, "w"))
+    assert bench.memory_read_bytes("gather") is None
+    assert bench.memory_read_bytes("hash") == rec["hash"]["bytes_per_launch"]
