@@ -211,7 +211,11 @@ def time_fused_weight(eg, dev, H: int, reps: int = 50) -> dict:
     we = (1 + 0.1 * torch.randn(H, generator=g)).to(dev)
     w = torch.empty((H,), dtype=torch.float64, device=dev)
     us = avg_launch_us(eg.bind_fused_weight(wh, we, w), reps)
-    return {"H": H, "us": us, "bytes": 16 * H}
+    gbps = 16 * H / (us * 1e3)
+    return {"H": H, "us": us, "bytes": 16 * H,
+            "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": gbps / HBM_PEAK_GBPS, "traffic": None,
+                         "note": f"one launch moves {16 * H} bytes; its time is launch latency"}}
 
 
 WIDTHS = (2048, 3072, 4096, 5120, 6144, 7168, 8192)
