@@ -130,11 +130,24 @@ def avg_launch_us(fn, reps: int) -> float:
     return 1e3 * a.elapsed_time(b) / reps
 
 
-def time_workload(w: Workload, steps: int, warmup: int) -> dict:
+def time_workload(w: Workload, steps: int, warmup: int, min_warmup_ms: float = 0.0) -> dict:
+    """`warmup` untimed steps, then `steps` timed ones. With min_warmup_ms,
+    warm-up continues until that much GPU time has passed: after the GPU has
+    idled (while the host generates a workload) its first ~10 ms of work run
+    up to 25% slow, which is tens of steps at the shorter workloads."""
     import torch
-    for _ in range(warmup):
-        w.step()
-    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    done, elapsed = 0, 0.0
+    while done < warmup or elapsed < min_warmup_ms:
+        batch = warmup - done if done < warmup else max(warmup, 1)
+        for _ in range(batch):
+            w.step()
+        done += batch
+        b.record()
+        torch.cuda.synchronize()
+        elapsed = a.elapsed_time(b)
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
@@ -153,7 +166,7 @@ def time_workload(w: Workload, steps: int, warmup: int) -> dict:
     ab = algorithmic_bytes(T, H)
     return {
         "workload": w.c.name, "T": T, "H": H, "P": w.P,
-        "ms_per_step": ms_step, "wall_s": wall,
+        "warmup_steps": done, "ms_per_step": ms_step, "wall_s": wall,
         "tokens_per_s": T / (ms_step / 1e3),
         "fwd": {"us": f_us, "tokens_per_s": T / (f_us / 1e6), "bytes": ab["fwd"],
                 "GBps": ab["fwd"] / (f_us * 1e3), "frac": ab["fwd"] / (f_us * 1e3) / HBM_PEAK_GBPS},
@@ -693,7 +706,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", type=int, default=4, choices=[3, 4, 5],
                     help="main workload (3: T=16384 H=4096, 4: T=32768 H=7168, 5: stress)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -771,7 +784,7 @@ def main():
         other = 3 if args.workload != 3 else 4
         print(f"[bench] generating workload {other}", file=sys.stderr, flush=True)
         w2 = Workload(other, dev, eg)
-        secondary = time_workload(w2, args.steps, args.warmup)
+        secondary = time_workload(w2, args.steps, args.warmup, min_warmup_ms=50.0)
         w2.free()
         del w2
         torch.cuda.empty_cache()
@@ -781,7 +794,7 @@ def main():
         if args.workload != 5:
             print("[bench] generating workload 5 (stress, T=65537)", file=sys.stderr, flush=True)
             w5 = Workload(5, dev, eg)
-            stress = time_workload(w5, min(args.steps, 20), args.warmup)
+            stress = time_workload(w5, min(args.steps, 20), args.warmup, min_warmup_ms=50.0)
             w5.free()
             del w5
             torch.cuda.empty_cache()

@@ -740,21 +740,21 @@ Plan generic_plan(int nchunk) {
 // W and C), so the backward's recomputed gate has the forward's bits.
 Plan fwd_plan(int nchunk) {
   if (nchunk == 896) return {7, 2, 2, true, false, 224};   // H = 7168
-  if (nchunk == 512) return {4, 2, 2, true, false, 256};   // H = 4096
-  if (nchunk == 640) return {5, 2, 2, true, false, 256};   // H = 5120
+  if (nchunk == 512) return {2, 4, 3, true, false, 256};   // H = 4096
+  if (nchunk == 640) return {2, 5, 3, true, false, 256};   // H = 5120
   if (nchunk == 384) return {3, 2, 3, true, false, 256};   // H = 3072
   if (nchunk == 256) return {1, 4, 2, true, false, 512};   // H = 2048
-  if (nchunk == 768) return {3, 4, 2, true, false, 256};   // H = 6144
+  if (nchunk == 768) return {2, 6, 2, true, false, 256};   // H = 6144
   return generic_plan(nchunk);
 }
 
 Plan bwd_plan(int nchunk) {
   if (nchunk == 896) return {7, 2, 3, true, true, 224};    // H = 7168
-  if (nchunk == 512) return {4, 2, 2, true, false, 256};   // H = 4096
-  if (nchunk == 640) return {5, 2, 2, true, false, 256};   // H = 5120
+  if (nchunk == 512) return {2, 4, 2, true, false, 256};   // H = 4096
+  if (nchunk == 640) return {2, 5, 2, true, true, 256};    // H = 5120
   if (nchunk == 384) return {3, 2, 2, true, false, 256};   // H = 3072
   if (nchunk == 256) return {1, 4, 2, true, false, 512};   // H = 2048
-  if (nchunk == 768) return {3, 4, 2, true, true, 256};    // H = 6144
+  if (nchunk == 768) return {2, 6, 2, true, true, 256};    // H = 6144
   return generic_plan(nchunk);
 }
 
@@ -795,11 +795,11 @@ tk_status run_fwd(FwdArgs a, int grid, hipStream_t st) {
 
 tk_status dispatch_fwd(const Plan& p, const FwdArgs& a, int grid, hipStream_t st) {
   if (p.W == 7 && p.C == 2 && p.full && p.D == 2) return run_fwd<7, 2, true, 2>(a, grid, st);
-  if (p.W == 4 && p.C == 2 && p.full && p.D == 2) return run_fwd<4, 2, true, 2>(a, grid, st);
-  if (p.W == 5 && p.C == 2 && p.full && p.D == 2) return run_fwd<5, 2, true, 2>(a, grid, st);
+  if (p.W == 2 && p.C == 4 && p.full && p.D == 3) return run_fwd<2, 4, true, 3>(a, grid, st);
+  if (p.W == 2 && p.C == 5 && p.full && p.D == 3) return run_fwd<2, 5, true, 3>(a, grid, st);
   if (p.W == 3 && p.C == 2 && p.full && p.D == 3) return run_fwd<3, 2, true, 3>(a, grid, st);
   if (p.W == 1 && p.C == 4 && p.full && p.D == 2) return run_fwd<1, 4, true, 2>(a, grid, st);
-  if (p.W == 3 && p.C == 4 && p.full && p.D == 2) return run_fwd<3, 4, true, 2>(a, grid, st);
+  if (p.W == 2 && p.C == 6 && p.full && p.D == 2) return run_fwd<2, 6, true, 2>(a, grid, st);
   if (p.D == 2 && p.C == 1) {
     switch (p.W) {
       case 1: return run_fwd<1, 1, false, 2>(a, grid, st);
@@ -836,16 +836,16 @@ tk_status run_bwd(BwdArgs a, int grid, hipStream_t st) {
 tk_status dispatch_bwd(const Plan& p, const BwdArgs& a, int grid, hipStream_t st) {
   if (p.W == 7 && p.C == 2 && p.full && p.D == 3 && p.wlds)
     return run_bwd<7, 2, true, 3, true>(a, grid, st);
-  if (p.W == 4 && p.C == 2 && p.full && p.D == 2 && !p.wlds)
-    return run_bwd<4, 2, true, 2, false>(a, grid, st);
-  if (p.W == 5 && p.C == 2 && p.full && p.D == 2 && !p.wlds)
-    return run_bwd<5, 2, true, 2, false>(a, grid, st);
+  if (p.W == 2 && p.C == 4 && p.full && p.D == 2 && !p.wlds)
+    return run_bwd<2, 4, true, 2, false>(a, grid, st);
+  if (p.W == 2 && p.C == 5 && p.full && p.D == 2 && p.wlds)
+    return run_bwd<2, 5, true, 2, true>(a, grid, st);
   if (p.W == 3 && p.C == 2 && p.full && p.D == 2 && !p.wlds)
     return run_bwd<3, 2, true, 2, false>(a, grid, st);
   if (p.W == 1 && p.C == 4 && p.full && p.D == 2 && !p.wlds)
     return run_bwd<1, 4, true, 2, false>(a, grid, st);
-  if (p.W == 3 && p.C == 4 && p.full && p.D == 2 && p.wlds)
-    return run_bwd<3, 4, true, 2, true>(a, grid, st);
+  if (p.W == 2 && p.C == 6 && p.full && p.D == 2 && p.wlds)
+    return run_bwd<2, 6, true, 2, true>(a, grid, st);
   if (p.D == 2 && !p.wlds && p.C == 1) {
     switch (p.W) {
       case 1: return run_bwd<1, 1, false, 2, false>(a, grid, st);

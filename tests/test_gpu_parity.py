@@ -393,8 +393,8 @@ def test_row_magnitudes_across_the_bf16_range(eg, cuda_device, H):
     (where the gate is 1/2) to 2^125, near the top of the bf16 range. The
     sums are fp64 and every coefficient is formed from normalised rows, so
     nothing overflows on the way; every row of every output is compared with
-    the oracle on its own. The widths cover each kind of plan: 4 x 2 and
-    1 x 4 with weights in registers, 7 x 2 and 3 x 4 with weights in LDS."""
+    the oracle on its own. The widths cover each kind of plan: 2 x 4 and
+    1 x 4 with weights in registers, 7 x 2 and 2 x 6 with weights in LDS."""
     exps = (-120, -64, -40, -20, 0, 20, 40, 56, 60, 64, 80, 100, 120, 125)
     cases = [(e, w) for e in exps for w in ("x", "k", "both", "v")]
 
@@ -588,9 +588,11 @@ def test_graph_capture_and_replay(eg, cuda_device):
 @pytest.mark.parametrize("T,H", [(20001, 3072), (8192, 8192), (24001, 2048), (9001, 5120),
                                  (6001, 6144)])
 def test_other_widths_many_rows_per_block(eg, cuda_device, T, H):
-    # the plans of the other widths (H=2048, 3072, 5120: full rows on 2, 3, 5
-    # waves; H=6144: masked tail chunks on 8 waves; H=8192: 8 waves x 2
-    # chunks) with ~25-80 rows per workgroup, compared on every element
+    # the plans of the other widths (H=2048: 1 wave x 4 chunks on 512
+    # workgroups; H=3072: 3 waves x 2 chunks; H=5120 and 6144: 2 waves x 5
+    # and x 6 chunks, weights in LDS in the backward; H=8192: 8 waves x 2
+    # chunks with the tail mask) with ~25-80 rows per workgroup, compared on
+    # every element
     d = make_case(T, H, seed=T + H)
     g = run_gpu(eg, d, cuda_device)
     assert_report(compare(d, g), name=f"T={T} H={H}")
