@@ -139,3 +139,47 @@ def test_gather_rejects_a_non_contiguous_index_tensor(eg, cuda_device):
     torch.cuda.synchronize()
     assert np.array_equal(bits(out), oracle.engram_gather(np.zeros((2, 2), np.int32),
                                                           bits(data), off, rows))
+
+
+def test_memory_read_in_a_hip_graph(eg, cuda_device):
+    """The hash and the gather allocate nothing either: hash -> gather captured
+    in a HIP graph replays bit for bit like the eager calls, with eager
+    writes to the outputs between the replays."""
+    import torch
+    dev = cuda_device
+    hc = synth.HASH_CONFIGS["tiny"]
+    hp = synth.hash_params(hc)
+    tokens = torch.from_numpy(synth.hash_tokens(hc)).to(dev)
+    sizes = hp["table_size"].reshape(-1)
+    Q, width = len(sizes), 24
+    table = torch.empty((Q * int(sizes.max()), width), dtype=torch.bfloat16, device=dev)
+    offsets = np.arange(Q, dtype=np.int64) * int(sizes.max())
+    for q in range(Q):
+        synth.fill_table_bits_torch(table, q, int(offsets[q]), int(sizes[q]), width)
+    idx = torch.empty((hc.B, hc.S, len(hc.ngram), hc.tables), dtype=torch.int32, device=dev)
+    rows = torch.empty((hc.B, hc.S, Q, width), dtype=torch.bfloat16, device=dev)
+
+    def read():
+        eg.tk_engram_hash(tokens, hp["ngram"], hp["mult"], hp["table_size"], hp["pad"], idx)
+        eg.tk_engram_gather(idx.view(hc.B, hc.S, Q), table, offsets, sizes, rows)
+
+    read()
+    torch.cuda.synchronize()
+    ref = [idx.clone(), rows.clone()]
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        read()                                   # warm-up on the capture stream
+    torch.cuda.current_stream(dev).wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        read()
+    for i in range(4):
+        idx.fill_(-7)                            # eager work between replays
+        rows.view(torch.int16).fill_(0x7FC1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(idx, ref[0]), i
+        assert torch.equal(rows.view(torch.int16), ref[1].view(torch.int16)), i
