@@ -267,6 +267,222 @@ def time_widths(eg, dev, reps: int = 30) -> list:
     return res
 
 
+PLACEMENT_GAPS = (0, 16, 256, 4096, 65536, 1 << 21)
+FOOTPRINT_TOKENS = (8192, 16384, 32768, 49152, 65536, 65537, 131072)
+
+
+def _best_us(fn, reps: int, tries: int = 3) -> float:
+    return min(avg_launch_us(fn, reps) for _ in range(tries))
+
+
+def placement_layouts(S: int) -> list:
+    """Placements of the backward's seven [T, H] streams (grad_out, x, k, v,
+    dx, dk, dv; S bytes each): a label and, per stream, (buffer, byte offset),
+    each buffer one allocation."""
+    four = 4096
+    lay = [("separate allocations", [(i, 0) for i in range(7)])]
+    for gap in PLACEMENT_GAPS:
+        lay.append((f"one buffer, gap {gap} B", [(0, i * (S + gap)) for i in range(7)]))
+    lay.append(("inputs separate, outputs one buffer gap 4096 B",
+                [(i, 0) for i in range(4)] + [(4, i * (S + four)) for i in range(3)]))
+    lay.append(("inputs one buffer gap 4096 B, outputs separate",
+                [(0, i * (S + four)) for i in range(4)] + [(i, 0) for i in range(1, 4)]))
+    lay.append(("one buffer, inputs gap 0, outputs gap 0, outputs shifted 4096 B",
+                [(0, i * S + (four if i >= 4 else 0)) for i in range(7)]))
+    return lay
+
+
+def time_placement(eg, dev, T: int = 32768, H: int = 7168, reps: int = 20,
+                   rounds: int = 2) -> list:
+    """Where a kernel's streams lie in HBM, against its time. The seven
+    [T, H] bf16 tensors of the backward (grad_out, x, k, v in; dx, dk, dv
+    out) are placed as placement_layouts lists: in separate allocations (2 MiB
+    aligned, the caching allocator's default), or as views into shared
+    buffers at staggered offsets. Each placement times the backward and the
+    forward (x, k, v in, out) kernels, and the stream probe with the same
+    mixes (4 reads + 3 writes, 3 + 1) on the same views. Inputs are seeded
+    normals. The sweep runs `rounds` times, the second in reverse order; one
+    record per placement and round; every figure is the best of three
+    averages over `reps` back-to-back launches."""
+    import torch
+    S = 2 * T * H
+    bf = torch.bfloat16
+    g = torch.Generator(device=dev).manual_seed(7)
+    wh = 1 + 0.1 * torch.randn(H, device=dev, generator=g)
+    we = 1 + 0.1 * torch.randn(H, device=dev, generator=g)
+    gate = torch.empty((T,), device=dev)
+    P = eg.tk_engram_num_partials(T, H)
+    ws = torch.empty((P, H), device=dev)
+    ab = algorithmic_bytes(T, H)
+
+    def measure(views, label, rnd):
+        go, x, k, v, dx, dk, dv = views
+        for t in (go, x, k, v):
+            t.normal_(generator=g)
+        fwd = eg.bind_gate_fwd(x, k, v, wh, we, dx, gate)
+        bwd = eg.bind_gate_bwd(go, x, k, v, wh, we, dx, dk, dv, ws)
+        as_i32 = [t.view(-1).view(torch.int32) for t in views]
+        p43 = (lambda: eg.tk_engram_stream_probe(as_i32[:4], as_i32[4:]))
+        p31 = (lambda: eg.tk_engram_stream_probe(as_i32[1:4], as_i32[4:5]))
+        b_us, f_us = _best_us(bwd, reps), _best_us(fwd, reps)
+        p43_us, p31_us = _best_us(p43, reps), _best_us(p31, reps)
+        rec = {"placement": label, "round": rnd, "T": T, "H": H,
+               "bwd_us": b_us, "bwd_frac": ab["bwd"] / (b_us * 1e3) / HBM_PEAK_GBPS,
+               "fwd_us": f_us, "fwd_frac": ab["fwd"] / (f_us * 1e3) / HBM_PEAK_GBPS,
+               "probe_4r3w_frac": 7 * S / (p43_us * 1e3) / HBM_PEAK_GBPS,
+               "probe_3r1w_frac": 4 * S / (p31_us * 1e3) / HBM_PEAK_GBPS}
+        print(f"[bench] placement {label} (round {rnd}): bwd {rec['bwd_frac']:.3f} "
+              f"fwd {rec['fwd_frac']:.3f} probe 4r3w {rec['probe_4r3w_frac']:.3f} "
+              f"3r1w {rec['probe_3r1w_frac']:.3f}", file=sys.stderr, flush=True)
+        return rec
+
+    # the GPU's first ~10 ms after idling run slow
+    warm = torch.empty(2 * T * H, dtype=bf, device=dev)
+    t_end = time.perf_counter() + 0.2
+    while time.perf_counter() < t_end:
+        eg.tk_engram_copy_probe(warm[: T * H], warm[T * H:])
+        torch.cuda.synchronize()
+    del warm
+    res = []
+    layouts = placement_layouts(S)
+    for rnd in range(rounds):
+        for label, spec in (layouts if rnd % 2 == 0 else layouts[::-1]):
+            size = {}
+            for b, off in spec:
+                size[b] = max(size.get(b, 0), off + S)
+            bufs = {b: torch.empty(n // 2, dtype=bf, device=dev) for b, n in size.items()}
+            views = [bufs[b][off // 2:(off + S) // 2].view(T, H) for b, off in spec]
+            res.append(measure(views, label, rnd))
+            del views, bufs
+            torch.cuda.empty_cache()
+    return res
+
+
+def time_footprint(eg, dev, H: int = 7168, reps: int = 10) -> list:
+    """The backward kernel and its 4-read, 3-write probe against the token
+    count (the footprint of the seven tensors), on seeded normals in separate
+    allocations, at H = 7168."""
+    import torch
+    res = []
+    g = torch.Generator(device=dev).manual_seed(11)
+    wh = 1 + 0.1 * torch.randn(H, device=dev, generator=g)
+    we = 1 + 0.1 * torch.randn(H, device=dev, generator=g)
+    for T in FOOTPRINT_TOKENS:
+        ts = [torch.empty((T, H), dtype=torch.bfloat16, device=dev) for _ in range(7)]
+        for t in ts[:4]:
+            t.normal_(generator=g)
+        P = eg.tk_engram_num_partials(T, H)
+        ws = torch.empty((P, H), device=dev)
+        bwd = eg.bind_gate_bwd(*ts[:4], wh, we, *ts[4:], ws)
+        as_i32 = [t.view(-1).view(torch.int32) for t in ts]
+        t_end = time.perf_counter() + 0.1
+        while time.perf_counter() < t_end:
+            bwd()
+            torch.cuda.synchronize()
+        b_us = _best_us(bwd, reps)
+        p_us = _best_us(lambda: eg.tk_engram_stream_probe(as_i32[:4], as_i32[4:]), reps)
+        ab = algorithmic_bytes(T, H)["bwd"]
+        rec = {"T": T, "H": H, "footprint_GB": 14 * T * H / 1e9, "bwd_us": b_us,
+               "bwd_frac": ab / (b_us * 1e3) / HBM_PEAK_GBPS,
+               "probe_4r3w_frac": 14 * T * H / (p_us * 1e3) / HBM_PEAK_GBPS}
+        print(f"[bench] footprint T={T}: bwd {rec['bwd_frac']:.3f} probe {rec['probe_4r3w_frac']:.3f}",
+              file=sys.stderr, flush=True)
+        res.append(rec)
+        del ts, ws, bwd, as_i32
+        torch.cuda.empty_cache()
+    return res
+
+
+FOOTPRINT_COUNTER_TOKENS = (32768, 65536, 131072)
+FOOTPRINT_COUNTER_LAUNCHES = 3
+
+
+def footprint_counter_run(eg, dev, H: int = 7168) -> dict:
+    """A fixed sequence of launches for rocprofv3 --pmc runs: one copy probe
+    of 2 x 32768 x H bf16 (the byte counters' calibration), then for each
+    token count of FOOTPRINT_COUNTER_TOKENS, FOOTPRINT_COUNTER_LAUNCHES
+    backward kernels followed by as many 4-read, 3-write stream probes on the
+    same seven tensors. footprint_from_counters attributes the dispatches by
+    this order."""
+    import torch
+    g = torch.Generator(device=dev).manual_seed(11)
+    wh = 1 + 0.1 * torch.randn(H, device=dev, generator=g)
+    we = 1 + 0.1 * torch.randn(H, device=dev, generator=g)
+    src = torch.empty(32768 * H, dtype=torch.bfloat16, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    eg.tk_engram_copy_probe(src, dst)
+    torch.cuda.synchronize()
+    del src, dst
+    out = {"H": H, "tokens": list(FOOTPRINT_COUNTER_TOKENS), "launches": FOOTPRINT_COUNTER_LAUNCHES}
+    for T in FOOTPRINT_COUNTER_TOKENS:
+        ts = [torch.empty((T, H), dtype=torch.bfloat16, device=dev) for _ in range(7)]
+        for t in ts[:4]:
+            t.normal_(generator=g)
+        ws = torch.empty((eg.tk_engram_num_partials(T, H), H), device=dev)
+        bwd = eg.bind_gate_bwd(*ts[:4], wh, we, *ts[4:], ws)
+        as_i32 = [t.view(-1).view(torch.int32) for t in ts]
+        for _ in range(FOOTPRINT_COUNTER_LAUNCHES):
+            bwd()
+        for _ in range(FOOTPRINT_COUNTER_LAUNCHES):
+            eg.tk_engram_stream_probe(as_i32[:4], as_i32[4:])
+        torch.cuda.synchronize()
+        print(f"[bench] footprint counters T={T} done", file=sys.stderr, flush=True)
+        del ts, ws, bwd, as_i32
+        torch.cuda.empty_cache()
+    return out
+
+
+def footprint_from_counters(csvs: list, H: int = 7168) -> dict:
+    """Per token count, the mean per dispatch of every counter in the given
+    rocprofv3 --pmc runs of --footprint-counters, for the backward kernel and
+    the stream probe; FETCH_SIZE and WRITE_SIZE also as bytes (scaled by
+    their reading for the copy probe) over the algorithmic bytes. Written to
+    profiles/footprint_counters_h<H>.json."""
+    import csv
+    n = FOOTPRINT_COUNTER_LAUNCHES
+    rec = {"H": H, "tokens": list(FOOTPRINT_COUNTER_TOKENS), "launches_each": n, "runs": []}
+    table = {}
+    for path in csvs:
+        names = sorted({r["Counter_Name"] for r in csv.DictReader(open(path))})
+        rec["runs"].append({"file": os.path.basename(os.path.dirname(path)) or path,
+                            "counters": names})
+        for counter in names:
+            rows = _per_dispatch(path, counter)
+            cp = [v for _, k, _, v in rows if k == "copy_probe_kernel"]
+            bw = [v for _, k, _, v in rows if k == "gate_bwd_kernel"]
+            pr = [v for _, k, _, v in rows if k == "stream_probe_kernel"]
+            if len(bw) != n * len(FOOTPRINT_COUNTER_TOKENS) or len(pr) != len(bw) or len(cp) != 1:
+                raise SystemExit(f"{path}: unexpected dispatch counts {len(cp)}, {len(bw)}, "
+                                 f"{len(pr)} for {counter}")
+            scale = None
+            if counter in ("FETCH_SIZE", "WRITE_SIZE"):
+                scale = 2 * 32768 * H / (1024.0 * cp[0])
+                rec[f"{counter.lower()}_scale"] = scale
+            for i, T in enumerate(FOOTPRINT_COUNTER_TOKENS):
+                for kern, vals in (("gate_bwd_kernel", bw), ("stream_probe_kernel", pr)):
+                    m = float(np.mean(vals[i * n:(i + 1) * n]))
+                    d = table.setdefault(str(T), {}).setdefault(kern, {})
+                    d[counter] = m
+                    if scale is not None:
+                        d[counter.lower() + "_bytes"] = m * 1024.0 * scale
+    for T, kk in table.items():
+        for kern, d in kk.items():
+            if "fetch_size_bytes" in d and "write_size_bytes" in d:
+                algo = 14 * int(T) * H
+                d["measured_over_algorithmic"] = (d["fetch_size_bytes"] + d["write_size_bytes"]) / algo
+            if "TCP_UTCL1_TRANSLATION_MISS_sum" in d and "TCP_UTCL1_REQUEST_sum" in d:
+                d["utcl1_miss_per_request"] = (d["TCP_UTCL1_TRANSLATION_MISS_sum"]
+                                               / max(1.0, d["TCP_UTCL1_REQUEST_sum"]))
+                d["utcl1_miss_per_MiB"] = (d["TCP_UTCL1_TRANSLATION_MISS_sum"]
+                                           / (14 * int(T) * H / 2 ** 20))
+    rec["per_tokens"] = table
+    path = os.path.join(PROFILES, f"footprint_counters_h{H}.json")
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1, sort_keys=True)
+        f.write("\n")
+    return rec
+
+
 def time_graph_step(eg, dev, T: int = 1024, H: int = 4096, reps: int = 50) -> dict:
     """One step (forward, backward, reduction) on a short batch, called eagerly
     through the Python binding and replayed from a captured HIP graph; the
@@ -721,6 +937,18 @@ def main():
                          "way, the counters' calibration), the N-gram hash and the table "
                          "gather on uniform and Zipf(1) token ids (one JSON line); for "
                          "rocprofv3 counter runs")
+    ap.add_argument("--placement", action="store_true",
+                    help="instead of the default run, time the gate kernels and the stream "
+                         "probe with their tensors at staggered offsets in one buffer and in "
+                         "separate allocations, then the backward against its footprint "
+                         "(one JSON line per measurement)")
+    ap.add_argument("--footprint-counters", action="store_true",
+                    help="instead of the default run, launch the backward and its stream "
+                         "probe a fixed number of times at T = "
+                         + ", ".join(map(str, FOOTPRINT_COUNTER_TOKENS))
+                         + " (H = 7168), for rocprofv3 --pmc runs")
+    ap.add_argument("--footprint-from", nargs="+", metavar="CSV",
+                    help="summarise rocprofv3 --pmc runs of --footprint-counters")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="summarise two rocprofv3 --pmc runs instead of benchmarking")
     ap.add_argument("--memory-read-traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -733,6 +961,9 @@ def main():
     if args.memory_read_traffic_from:
         rec = memory_read_traffic(*args.memory_read_traffic_from)
         print(json.dumps(rec, indent=1, sort_keys=True))
+        return
+    if args.footprint_from:
+        print(json.dumps(footprint_from_counters(args.footprint_from), indent=1, sort_keys=True))
         return
     if args.valu_from:
         print(json.dumps(valu_from_counters(args.valu_from), indent=1, sort_keys=True))
@@ -756,6 +987,15 @@ def main():
     if args.widths:
         for r in time_widths(eg, dev):
             print(json.dumps(r))
+        return
+    if args.placement:
+        for r in time_placement(eg, dev):
+            print(json.dumps(r), flush=True)
+        for r in time_footprint(eg, dev):
+            print(json.dumps(r), flush=True)
+        return
+    if args.footprint_counters:
+        print(json.dumps(footprint_counter_run(eg, dev)), flush=True)
         return
     if args.memory_read:
         import synth

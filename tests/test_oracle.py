@@ -363,6 +363,74 @@ def test_round_bf16_brute_force_on_doubles():
     assert np.all(err <= np.abs(up - v)) and np.all(err <= np.abs(dn - v))
 
 
+def _nearest_bf16(v):
+    """bf16 bits of fp64 values by IEEE 754 round-to-nearest-even, found by
+    searching the table of every finite bf16 value: the nearest one wins,
+    a tie goes to the pattern with an even last bit, and a magnitude of at
+    least 2^128 - 2^119 (halfway from the largest finite value, 0x7F7F, to
+    2^128) rounds to infinity. NaN is not handled."""
+    pats = np.arange(0, 0x7F80, dtype=np.uint32)            # +0 up to 0x7F7F
+    vals = (pats << 16).view(np.float32).astype(np.float64)  # increasing
+    a = np.abs(np.asarray(v, dtype=np.float64))
+    hi = np.minimum(np.searchsorted(vals, a), len(vals) - 1)
+    lo = np.maximum(hi - 1, 0)
+    d_lo, d_hi = np.abs(a - vals[lo]), np.abs(vals[hi] - a)
+    pick = np.where(d_lo < d_hi, lo, np.where(d_hi < d_lo, hi, np.where(hi % 2 == 0, hi, lo)))
+    pick = np.where(a == vals[hi], hi, pick)
+    out = pats[pick].astype(np.uint32)
+    out = np.where(a >= 2.0 ** 128 - 2.0 ** 119, 0x7F80, out)
+    return (out | np.where(np.signbit(v), 0x8000, 0)).astype(np.uint16)
+
+
+def test_nearest_bf16_reference_on_known_values():
+    # the search above, on values whose bf16 patterns follow from the format
+    vals = [1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, 2.0 ** -133, 1.5 * 2 ** -133,
+            2.5 * 2 ** -133, 0.5 * 2 ** -133, 0.75 * 2 ** -133, 2.0 ** -126 - 2 ** -134,
+            2.0 ** 127 * (2 - 2 ** -7), 2.0 ** 128 - 2.0 ** 119, 2.0 ** 130, -0.0, -1.0]
+    want = [0x3F80, 0x3F80, 0x3F82, 0x0001, 0x0002, 0x0002, 0x0000, 0x0001, 0x0080,
+            0x7F7F, 0x7F80, 0x7F80, 0x8000, 0xBF80]
+    assert _nearest_bf16(np.array(vals)).tolist() == want
+
+
+def test_round_bf16_across_the_whole_range():
+    # |v| from 2^-140 to 2^129: the subnormal bf16 range (multiples of
+    # 2^-133, their exact ties and the values next to them), every binade of
+    # the normal range, and the top: the largest finite bf16 (0x7F7F), the
+    # midpoint to infinity and what lies on either side of both.
+    r = np.random.default_rng(43)
+    e = np.arange(-140, 130)
+    sig = np.concatenate([[1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, 2 - 2 ** -8, 2 - 2 ** -9],
+                          1.0 + r.random(60), 1.0 + r.integers(0, 2 ** 23, 60) * 2.0 ** -23])
+    v = (sig[None, :] * 2.0 ** e[:, None]).ravel()
+    q = 2.0 ** -133
+    j = np.arange(0, 129, dtype=np.float64)
+    sub = np.concatenate([j * q, (j + 0.5) * q, (j + 0.25) * q, (j + 0.75) * q])
+    top_max = 2.0 ** 127 * (2 - 2 ** -7)           # 0x7F7F
+    top_mid = 2.0 ** 128 - 2.0 ** 119                # halfway to 2^128
+    top = np.array([top_max, top_mid, 2.0 ** 128, 2.0 ** 129, np.finfo(np.float64).max])
+    v = np.concatenate([v, sub, top])
+    with np.errstate(over="ignore"):
+        near = np.concatenate([np.nextafter(v, 0.0), np.nextafter(v, np.inf)])
+    v = np.concatenate([v, near])
+    v = v[(v >= 2.0 ** -141) | (v == 0.0)]
+    v = np.concatenate([v, -v])
+    got = oracle.round_bf16(v)
+    assert np.array_equal(got, _nearest_bf16(v))
+    assert got[np.argmax(v == top_mid)] == 0x7F80
+    assert got[np.argmax(v == np.nextafter(top_mid, 0.0))] == 0x7F7F
+    # torch's fp32 -> bf16 on the values fp32 holds exactly, ties included
+    with np.errstate(over="ignore"):
+        f32 = v.astype(np.float32)
+    exact = np.isfinite(f32) & (f32.astype(np.float64) == v)
+    want = (torch.from_numpy(f32[exact]).to(torch.bfloat16).view(torch.int16).numpy()
+            .view(np.uint16))
+    assert exact.sum() > 20000
+    assert np.array_equal(got[exact], want)
+    # infinities keep their sign, and NaN gives the quiet NaN
+    special = oracle.round_bf16(np.array([np.inf, -np.inf, np.nan]))
+    assert special.tolist() == [0x7F80, 0xFF80, 0x7FC0]
+
+
 def test_oracle_snapshot_config1():
     # Regression record written by tests/golden/make_oracle_snapshot.py.
     import os

@@ -79,6 +79,15 @@ MUTANTS = [
      "(dropped > half || (dropped == half && (keep & 1)))", "(dropped >= half)"),
     ("rounding to the wrong kept width", "engram_oracle.cpp",
      "uint64_t keep = frac >> 45;", "uint64_t keep = frac >> 44;"),
+    ("overflow to infinity from 2^129 instead of 2^128", "engram_oracle.cpp",
+     "if (e > 127) return sbit | 0x7F80;", "if (e > 128) return sbit | 0x7F80;"),
+    ("rounding past the largest finite value saturates", "engram_oracle.cpp",
+     "if (biased >= 255) return (uint16_t)((sign << 15) | 0x7F80);",
+     "if (biased >= 255) return (uint16_t)((sign << 15) | 0x7F7F);"),
+    ("subnormal quantum 2^-134 instead of 2^-133", "engram_oracle.cpp",
+     "const double units = mag * 0x1p133;", "const double units = mag * 0x1p134;"),
+    ("subnormal ties rounded away from even", "engram_oracle.cpp",
+     "(frac > 0.5 || (frac == 0.5 && std::fmod(lo, 2.0) != 0.0))", "(frac >= 0.5)"),
     ("hash sums the products instead of XOR", "engram_hash_oracle.cpp",
      "h ^= (uint64_t)tok * a[i];", "h += (uint64_t)tok * a[i];"),
     ("hash window one position short at the start", "engram_hash_oracle.cpp",
