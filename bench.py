@@ -358,10 +358,15 @@ def time_placement(eg, dev, T: int = 32768, H: int = 7168, reps: int = 20,
     return res
 
 
+FOOTPRINT_SPLITS = (8192, 16384, 32768)
+
+
 def time_footprint(eg, dev, H: int = 7168, reps: int = 10) -> list:
     """The backward kernel and its 4-read, 3-write probe against the token
     count (the footprint of the seven tensors), on seeded normals in separate
-    allocations, at H = 7168."""
+    allocations, at H = 7168; and the same rows as back-to-back launches of
+    at most `split` rows each (views of the same tensors, each launch with a
+    workspace of its own), for each split of FOOTPRINT_SPLITS below T."""
     import torch
     res = []
     g = torch.Generator(device=dev).manual_seed(11)
@@ -384,8 +389,28 @@ def time_footprint(eg, dev, H: int = 7168, reps: int = 10) -> list:
         ab = algorithmic_bytes(T, H)["bwd"]
         rec = {"T": T, "H": H, "footprint_GB": 14 * T * H / 1e9, "bwd_us": b_us,
                "bwd_frac": ab / (b_us * 1e3) / HBM_PEAK_GBPS,
-               "probe_4r3w_frac": 14 * T * H / (p_us * 1e3) / HBM_PEAK_GBPS}
-        print(f"[bench] footprint T={T}: bwd {rec['bwd_frac']:.3f} probe {rec['probe_4r3w_frac']:.3f}",
+               "probe_4r3w_frac": 14 * T * H / (p_us * 1e3) / HBM_PEAK_GBPS, "split": {}}
+        for split in FOOTPRINT_SPLITS:
+            if split >= T:
+                continue
+            calls = []
+            for a in range(0, T, split):
+                n = min(split, T - a)
+                wsn = torch.empty((eg.tk_engram_num_partials(n, H), H), device=dev)
+                calls.append(eg.bind_gate_bwd(*[t[a:a + n] for t in ts[:4]], wh, we,
+                                              *[t[a:a + n] for t in ts[4:]], wsn))
+
+            def run_all():
+                for c in calls:
+                    c()
+
+            s_us = _best_us(run_all, reps)
+            rec["split"][str(split)] = {"launches": len(calls), "us": s_us,
+                                        "frac": ab / (s_us * 1e3) / HBM_PEAK_GBPS}
+            del calls
+        print(f"[bench] footprint T={T}: bwd {rec['bwd_frac']:.3f} probe "
+              f"{rec['probe_4r3w_frac']:.3f} split "
+              + " ".join(f"{k}:{v['frac']:.3f}" for k, v in rec["split"].items()),
               file=sys.stderr, flush=True)
         res.append(rec)
         del ts, ws, bwd, as_i32
@@ -549,7 +574,10 @@ def time_hash(eg, dev, name: str = "b1024s4096", reps: int = 20) -> dict:
            "bytes": nbytes, "GBps": nbytes / (us * 1e3),
            "frac": nbytes / (us * 1e3) / HBM_PEAK_GBPS}
     if name == HASH_WORKLOAD[len("hash_"):]:
-        res["roofline"] = hash_valu_roofline(res["tokens_per_s"])
+        res["roofline"] = {"bound": "hbm", "achieved": res["GBps"], "peak": HBM_PEAK_GBPS,
+                           "unit": "GB/s", "frac": res["frac"],
+                           "traffic": memory_read_bytes("hash")}
+        res["valu_issue_note"] = hash_valu_note(res["tokens_per_s"])
     return res
 
 
@@ -710,13 +738,36 @@ def cpu_model() -> str:
     return "unknown"
 
 
+def host_cpu_share() -> dict:
+    """The host CPUs this process may use: the machine's count, the CPUs in
+    its affinity mask, and the cgroup CPU quota (cgroup v2 cpu.max) if one is
+    set. `threads` is the smaller of the last two: every CPU the process can
+    actually run on."""
+    total = os.cpu_count() or 1
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        affinity = total
+    quota = None
+    try:
+        with open("/sys/fs/cgroup/cpu.max") as f:
+            q, period = f.read().split()[:2]
+            if q != "max":
+                quota = int(q) / int(period)
+    except (OSError, ValueError):
+        pass
+    threads = affinity if quota is None else max(1, min(affinity, int(quota)))
+    return {"host_cpus": total, "affinity_cpus": affinity, "cgroup_cpu_quota": quota,
+            "threads": threads}
+
+
 def cpu_baseline(host: dict, budget_s: float = 10.0, side_s: float = 3.0) -> dict:
     """The fp64 oracle, as it stands, on the host cores. `value` is forward +
-    backward on every thread the oracle uses; beside it, the same on one
-    thread and the forward alone on every thread, each over a shorter
-    sample, with their algorithmic bytes per second."""
-    import oracle
-    th = oracle.default_threads()
+    backward on every CPU this process may use (host_cpu_share); beside it,
+    the same on one thread and the forward alone on every CPU, each over a
+    shorter sample, with their algorithmic bytes per second."""
+    share = host_cpu_share()
+    th = share["threads"]
     T, H = host["x"].shape
     ab = {key: b / T for key, b in algorithmic_bytes(T, H).items()}   # per token
     done, dt = _oracle_rate(host, th, budget_s, True)
@@ -727,6 +778,9 @@ def cpu_baseline(host: dict, budget_s: float = 10.0, side_s: float = 3.0) -> dic
             "sample": f"{done} tokens ({done / T:.2f} passes over the {T}-token workload, "
                       f"chunks of 4096), fp64 forward + backward incl. dwh/dwe, "
                       f"{dt:.1f} s wall on {th} threads",
+            "threads": th, "host_cpus": share["host_cpus"],
+            "affinity_cpus": share["affinity_cpus"],
+            "cgroup_cpu_quota": share["cgroup_cpu_quota"],
             "GBps_equiv": rate * (ab["fwd"] + ab["bwd"]) / 1e9,
             "single_thread": {"value": rate1, "sample": f"{done1} tokens, {dt1:.1f} s",
                               "GBps_equiv": rate1 * (ab["fwd"] + ab["bwd"]) / 1e9},
@@ -899,10 +953,11 @@ def memory_read_bytes(name: str):
     return rec[name]["bytes_per_launch"]
 
 
-def hash_valu_roofline(tokens_per_s: float):
-    """The hash's ALU roofline: tokens per second if every SIMD issued one
-    VALU instruction every 4 cycles, from the committed counter record of
-    the current hash source; None if that record is missing or stale."""
+def hash_valu_note(tokens_per_s: float):
+    """Not a roofline: tokens per second if every SIMD issued one VALU
+    instruction every 4 cycles, at the hash's own executed instruction count
+    from the committed counter record of the current hash source; None if
+    that record is missing or stale."""
     path = os.path.join(PROFILES, f"valu_{HASH_WORKLOAD}.json")
     try:
         rec = json.load(open(path))
@@ -910,12 +965,12 @@ def hash_valu_roofline(tokens_per_s: float):
         return None
     if rec.get("hash_source_sha256_16") != kernel_source_hash(HASH_SRC):
         return None
-    peak = VALU_WAVE_INSTS_PER_S * rec["tokens_per_wave"] / rec["valu_insts_per_wave"]
-    return {"bound": "alu", "achieved": tokens_per_s, "peak": peak, "unit": "tokens/s",
-            "frac": tokens_per_s / peak, "traffic": memory_read_bytes("hash"),
+    issue = VALU_WAVE_INSTS_PER_S * rec["tokens_per_wave"] / rec["valu_insts_per_wave"]
+    return {"tokens_per_s_at_valu_issue_rate": issue, "frac": tokens_per_s / issue,
             "basis": f"{rec['valu_insts_per_wave']:.0f} VALU instructions per wave of "
-                     f"{rec['tokens_per_wave']:.0f} tokens (rocprofv3 SQ_INSTS_VALU / "
-                     "SQ_WAVES), one per SIMD every 4 cycles, 1024 SIMDs at 2.4 GHz"}
+                     f"{rec['tokens_per_wave']:.0f} tokens as executed (rocprofv3 "
+                     "SQ_INSTS_VALU / SQ_WAVES), one per SIMD every 4 cycles, 1024 SIMDs "
+                     "at 2.4 GHz; the kernel's own count, so not a bound on the method"}
 
 
 def main():
@@ -942,6 +997,8 @@ def main():
                          "probe with their tensors at staggered offsets in one buffer and in "
                          "separate allocations, then the backward against its footprint "
                          "(one JSON line per measurement)")
+    ap.add_argument("--footprint-only", action="store_true",
+                    help="with --placement, run only its footprint sweep")
     ap.add_argument("--footprint-counters", action="store_true",
                     help="instead of the default run, launch the backward and its stream "
                          "probe a fixed number of times at T = "
@@ -989,8 +1046,9 @@ def main():
             print(json.dumps(r))
         return
     if args.placement:
-        for r in time_placement(eg, dev):
-            print(json.dumps(r), flush=True)
+        if not args.footprint_only:
+            for r in time_placement(eg, dev):
+                print(json.dumps(r), flush=True)
         for r in time_footprint(eg, dev):
             print(json.dumps(r), flush=True)
         return
@@ -1078,10 +1136,11 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16",
         "data": "synthetic (seeded Philox-4x32-10 inputs of the stated recipe)",
         "config": {"workload": main_res["workload"], "tokens": main_res["T"],
-                   "hidden": main_res["H"], "tensor_dtype": "bf16", "row_sums": "f64",
+                   "hidden": main_res["H"], "tensor_dtype": "bf16", "elementwise": "f32",
+                   "row_sums": "f64",
                    "step": "gate_fwd + gate_bwd + grad_w_reduce", "partials": main_res["P"]},
         "roofline": {"bound": "hbm", "kernel": "gate_bwd_kernel",
                      "achieved": bk["GBps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",

@@ -213,11 +213,26 @@ def tk_engram_grad_w_reduce(workspace, P, H, wh, we, dwh=None, dwe=None, stream=
     return dwh, dwe
 
 
+def _probe_tensors(tensors):
+    """The probes' tensors: contiguous, on one GPU, of one byte size."""
+    torch = _torch()
+    dev = tensors[0].device if isinstance(tensors[0], torch.Tensor) else None
+    if dev is None or dev.type != "cuda":
+        raise ValueError("probe tensors must be GPU tensors")
+    n = tensors[0].numel() * tensors[0].element_size()
+    for t in tensors:
+        if not isinstance(t, torch.Tensor) or t.device != dev:
+            raise ValueError(f"all probe tensors must be on {dev}")
+        if not t.is_contiguous() or t.numel() * t.element_size() != n:
+            raise ValueError("all probe tensors must be contiguous and of one byte size")
+    return dev, n
+
+
 def tk_engram_copy_probe(src, dst, stream=None):
     """Copy src into dst (same byte size) with the library's 128-bit copy."""
-    n = src.numel() * src.element_size()
-    if dst.numel() * dst.element_size() != n:
+    if src.numel() * src.element_size() != dst.numel() * dst.element_size():
         raise ValueError("src and dst differ in size")
+    _, n = _probe_tensors([src, dst])
     st = load_library().tk_engram_copy_probe(ctypes.c_void_p(src.data_ptr()),
                                              ctypes.c_void_p(dst.data_ptr()), n,
                                              _stream_handle(src.device, stream))
@@ -406,10 +421,7 @@ def tk_engram_stream_probe(srcs, dsts, stream=None):
     GPU tensors of one byte size) with the library's tiled probe kernel."""
     if not srcs or not dsts:
         raise ValueError("need at least one source and one destination")
-    n = srcs[0].numel() * srcs[0].element_size()
-    for t in list(srcs) + list(dsts):
-        if t.numel() * t.element_size() != n or not t.is_contiguous():
-            raise ValueError("all probe tensors must be contiguous and of one byte size")
+    _, n = _probe_tensors(list(srcs) + list(dsts))
     src = (ctypes.c_void_p * len(srcs))(*[t.data_ptr() for t in srcs])
     dst = (ctypes.c_void_p * len(dsts))(*[t.data_ptr() for t in dsts])
     st = load_library().tk_engram_stream_probe(

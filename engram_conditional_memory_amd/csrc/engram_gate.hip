@@ -717,6 +717,12 @@ tk_status check_shape(int64_t T, int64_t H) {
 
 bool finite_positive(double a) { return std::isfinite(a) && a > 0.0; }
 
+// The derivative clamp is applied in fp32: it must round to a normal fp32.
+bool fp32_normal(double a) {
+  const float f = (float)a;
+  return std::isfinite(f) && f >= 1.17549435e-38f;
+}
+
 // Launch plan for a row of nchunk 16-byte chunks: W waves per row, C chunks
 // per thread (FULL when W * 64 * C == nchunk, i.e. no masking), D rows in
 // flight per workgroup, weights in LDS (backward), and G workgroups walking
@@ -860,6 +866,63 @@ tk_status dispatch_bwd(const Plan& p, const BwdArgs& a, int grid, hipStream_t st
   return TK_ERR_UNSUPPORTED;
 }
 
+tk_status check_bwd_args(const uint16_t* grad_out, const uint16_t* x, const uint16_t* k,
+                         const uint16_t* v, const float* wh, const float* we,
+                         const uint16_t* dx, const uint16_t* dk, const uint16_t* dv,
+                         int64_t T, int64_t H, double eps, double dsqrt_clamp) {
+  tk_status st = check_shape(T, H);
+  if (st != TK_SUCCESS) return st;
+  if (!finite_positive(eps) || !fp32_normal(dsqrt_clamp)) return TK_ERR_VALUE;
+  if (T == 0) return TK_SUCCESS;
+  if (!grad_out || !x || !k || !v || !wh || !we || !dx || !dk || !dv) return TK_ERR_NULL;
+  if (!aligned16(grad_out) || !aligned16(x) || !aligned16(k) || !aligned16(v) ||
+      !aligned16(wh) || !aligned16(we) || !aligned16(dx) || !aligned16(dk) || !aligned16(dv))
+    return TK_ERR_ALIGN;
+  return TK_SUCCESS;
+}
+
+// The backward's launch once its arguments are checked; T > 0.
+tk_status enqueue_bwd(const uint16_t* grad_out, const uint16_t* x, const uint16_t* k,
+                      const uint16_t* v, const float* wh, const float* we, uint16_t* dx,
+                      uint16_t* dk, uint16_t* dv, float* partial, int64_t T, int64_t H,
+                      double eps, double dsqrt_clamp, hipStream_t st) {
+  const int nchunk = (int)(H / 8);
+  BwdArgs a;
+  a.g = reinterpret_cast<const u32x4*>(grad_out);
+  a.x = reinterpret_cast<const u32x4*>(x);
+  a.k = reinterpret_cast<const u32x4*>(k);
+  a.v = reinterpret_cast<const u32x4*>(v);
+  a.wh = reinterpret_cast<const f32x4*>(wh);
+  a.we = reinterpret_cast<const f32x4*>(we);
+  a.dx = reinterpret_cast<u32x4*>(dx);
+  a.dk = reinterpret_cast<u32x4*>(dk);
+  a.dv = reinterpret_cast<u32x4*>(dv);
+  a.partial = reinterpret_cast<f32x4*>(partial);
+  const Plan plan = bwd_plan(nchunk);
+  const int grid = (int)grid_of(plan, T);
+  a.walk = row_walk(T, grid);
+  a.nchunk = nchunk;
+  a.eps = eps;
+  a.clamp = (float)dsqrt_clamp;
+  a.inv_h = 1.0 / (double)H;
+  a.inv_sqrt_h = 1.0 / std::sqrt((double)H);
+  return dispatch_bwd(plan, a, grid, st);
+}
+
+// The reduction's launch once its arguments are checked.
+tk_status enqueue_reduce(const float* workspace, int64_t P, int64_t H, const float* wh,
+                         const float* we, float* dwh, float* dwe, hipStream_t st) {
+  const f32x4* ws = reinterpret_cast<const f32x4*>(workspace);
+  const f32x4* a = reinterpret_cast<const f32x4*>(wh);
+  const f32x4* b = reinterpret_cast<const f32x4*>(we);
+  f32x4* oh = reinterpret_cast<f32x4*>(dwh);
+  f32x4* oe = reinterpret_cast<f32x4*>(dwe);
+  int nq = (int)(H / 4);
+  void* args[] = {&ws, &P, &nq, &a, &b, &oh, &oe};
+  const int grid = (nq + kRedCols4 - 1) / kRedCols4;
+  return launch(grad_w_reduce_kernel, grid, kRedCols4 * kRedSlices, args, st);
+}
+
 }  // namespace
 
 extern "C" {
@@ -911,38 +974,13 @@ tk_status tk_engram_gate_bwd(const uint16_t* grad_out, const uint16_t* x,
                              uint16_t* dk, uint16_t* dv, float* workspace,
                              size_t workspace_bytes, int64_t T, int64_t H,
                              double eps, double dsqrt_clamp, void* stream) {
-  tk_status st = check_shape(T, H);
-  if (st != TK_SUCCESS) return st;
-  if (!finite_positive(eps) || !finite_positive(dsqrt_clamp)) return TK_ERR_VALUE;
-  if (T == 0) return TK_SUCCESS;
-  if (!grad_out || !x || !k || !v || !wh || !we || !dx || !dk || !dv || !workspace)
-    return TK_ERR_NULL;
-  if (!aligned16(grad_out) || !aligned16(x) || !aligned16(k) || !aligned16(v) ||
-      !aligned16(wh) || !aligned16(we) || !aligned16(dx) || !aligned16(dk) ||
-      !aligned16(dv) || !aligned16(workspace))
-    return TK_ERR_ALIGN;
+  tk_status st = check_bwd_args(grad_out, x, k, v, wh, we, dx, dk, dv, T, H, eps, dsqrt_clamp);
+  if (st != TK_SUCCESS || T == 0) return st;
+  if (!workspace) return TK_ERR_NULL;
+  if (!aligned16(workspace)) return TK_ERR_ALIGN;
   if (workspace_bytes < tk_engram_bwd_workspace_bytes(T, H)) return TK_ERR_WORKSPACE;
-  const int nchunk = (int)(H / 8);
-  BwdArgs a;
-  a.g = reinterpret_cast<const u32x4*>(grad_out);
-  a.x = reinterpret_cast<const u32x4*>(x);
-  a.k = reinterpret_cast<const u32x4*>(k);
-  a.v = reinterpret_cast<const u32x4*>(v);
-  a.wh = reinterpret_cast<const f32x4*>(wh);
-  a.we = reinterpret_cast<const f32x4*>(we);
-  a.dx = reinterpret_cast<u32x4*>(dx);
-  a.dk = reinterpret_cast<u32x4*>(dk);
-  a.dv = reinterpret_cast<u32x4*>(dv);
-  a.partial = reinterpret_cast<f32x4*>(workspace);
-  const Plan plan = bwd_plan(nchunk);
-  const int grid = (int)grid_of(plan, T);
-  a.walk = row_walk(T, grid);
-  a.nchunk = nchunk;
-  a.eps = eps;
-  a.clamp = (float)dsqrt_clamp;
-  a.inv_h = 1.0 / (double)H;
-  a.inv_sqrt_h = 1.0 / std::sqrt((double)H);
-  return dispatch_bwd(plan, a, grid, reinterpret_cast<hipStream_t>(stream));
+  return enqueue_bwd(grad_out, x, k, v, wh, we, dx, dk, dv, workspace, T, H, eps,
+                     dsqrt_clamp, reinterpret_cast<hipStream_t>(stream));
 }
 
 tk_status tk_engram_grad_w_reduce(const float* workspace, int64_t P, int64_t H,
@@ -951,20 +989,13 @@ tk_status tk_engram_grad_w_reduce(const float* workspace, int64_t P, int64_t H,
   if (P < 0) return TK_ERR_SHAPE;
   tk_status st = check_shape(0, H);
   if (st != TK_SUCCESS) return st;
+  if (P > TK_ENGRAM_MAX_PARTIALS) return TK_ERR_UNSUPPORTED;
   if ((P > 0 && !workspace) || !wh || !we || !dwh || !dwe) return TK_ERR_NULL;
   if ((P > 0 && !aligned16(workspace)) || !aligned16(wh) || !aligned16(we) ||
       !aligned16(dwh) || !aligned16(dwe))
     return TK_ERR_ALIGN;
-  const f32x4* ws = reinterpret_cast<const f32x4*>(workspace);
-  const f32x4* a = reinterpret_cast<const f32x4*>(wh);
-  const f32x4* b = reinterpret_cast<const f32x4*>(we);
-  f32x4* oh = reinterpret_cast<f32x4*>(dwh);
-  f32x4* oe = reinterpret_cast<f32x4*>(dwe);
-  int nq = (int)(H / 4);
-  void* args[] = {&ws, &P, &nq, &a, &b, &oh, &oe};
-  const int grid = (nq + kRedCols4 - 1) / kRedCols4;
-  return launch(grad_w_reduce_kernel, grid, kRedCols4 * kRedSlices, args,
-                reinterpret_cast<hipStream_t>(stream));
+  return enqueue_reduce(workspace, P, H, wh, we, dwh, dwe,
+                        reinterpret_cast<hipStream_t>(stream));
 }
 
 tk_status tk_engram_fused_weight(const float* wh, const float* we, double* w, int64_t H,

@@ -76,6 +76,8 @@ enum {
 
 #define TK_ENGRAM_ABI_VERSION 1
 #define TK_ENGRAM_MAX_H 8192
+/* Largest number of weight-gradient partial rows any (T, H) uses. */
+#define TK_ENGRAM_MAX_PARTIALS 512
 
 /*
  * Forward: zhichai.net TileKernels page, section "5. Engram", gate formula
@@ -120,7 +122,9 @@ size_t tk_engram_bwd_workspace_bytes(int64_t T, int64_t H);
  *   dsqrt_clamp     : the derivative of signed_sqrt, 1 / (2 sqrt|z|), is
  *                     evaluated as 1 / (2 sqrt(max(|z|, dsqrt_clamp))) so it
  *                     stays finite at z = 0 (the page gives no value there);
- *                     finite and > 0
+ *                     it is applied in fp32, so it must round to a normal
+ *                     positive fp32 value (2^-126 .. FLT_MAX), else
+ *                     TK_ERR_VALUE
  *
  * The gate is recomputed from x and k with the forward's arithmetic and
  * summation order, so it has the forward's bits and dv = bf16(gate * grad_out)
@@ -142,7 +146,10 @@ tk_status tk_engram_gate_bwd(const uint16_t* grad_out, const uint16_t* x,
  * since dL/dwh_i = sum_t dd_t r_x,t x_t,i * (r_k,t k_t,i we_i) and likewise
  * for we. P = 0 writes zeros.
  *
- *   workspace : fp32 [P, H], P = tk_engram_num_partials(T, H)
+ *   workspace : fp32 [P, H], P = tk_engram_num_partials(T, H); the call has
+ *               no size argument, so it trusts the caller that the buffer
+ *               holds P * H values
+ *   P         : 0 .. TK_ENGRAM_MAX_PARTIALS, else TK_ERR_UNSUPPORTED
  *   wh, we    : fp32 [H]
  *   dwh, dwe  : fp32 [H]
  */

@@ -18,6 +18,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(eg.LIBRARY_PATH),
 
 A16 = 0x10000          # a 16-byte-aligned fake device address (never dereferenced)
 A4 = 0x10004
+B_MAX_PARTIALS = 512   # TK_ENGRAM_MAX_PARTIALS
 
 
 def declared_functions():
@@ -111,6 +112,10 @@ def test_backward_argument_checks():
         assert bwd(**{name: A4}) == B.TK_ERR_ALIGN, name
     need = eg.tk_engram_bwd_workspace_bytes(4, 64)
     assert bwd(wsb=need - 4) == B.TK_ERR_WORKSPACE
+    # the clamp is applied in fp32 and must round to a normal fp32 value
+    for clamp in (1e-300, 1e-39, 1e-45, 1e39, -1e-4, float("nan")):
+        assert bwd(clamp=clamp) == B.TK_ERR_VALUE, clamp
+        assert bwd(clamp=clamp, T=0, ws=None, wsb=0) == B.TK_ERR_VALUE, clamp
 
 
 def test_reduce_argument_checks():
@@ -118,6 +123,7 @@ def test_reduce_argument_checks():
     assert red(H=-8) == B.TK_ERR_SHAPE
     assert red(H=36) == B.TK_ERR_ALIGN
     assert red(H=9000) == B.TK_ERR_UNSUPPORTED
+    assert red(P=B_MAX_PARTIALS + 1) == B.TK_ERR_UNSUPPORTED
     for name in ("ws", "wh", "we", "dwh", "dwe"):
         assert red(**{name: None}) == B.TK_ERR_NULL, name
         assert red(**{name: A4}) == B.TK_ERR_ALIGN, name
@@ -137,6 +143,16 @@ def test_binding_refuses_host_tensors():
     w = torch.ones(64)
     with pytest.raises(ValueError):
         eg.tk_engram_gate_fwd(x, x, x, w, w)
+
+
+def test_probe_bindings_refuse_host_tensors():
+    # a host pointer handed to a probe kernel would fault the GPU
+    import torch
+    a, b = torch.zeros(64, dtype=torch.int32), torch.zeros(64, dtype=torch.int32)
+    with pytest.raises(ValueError, match="GPU"):
+        eg.tk_engram_copy_probe(a, b)
+    with pytest.raises(ValueError, match="GPU"):
+        eg.tk_engram_stream_probe([a], [b])
 
 
 def test_missing_library_raises(tmp_path):

@@ -84,14 +84,14 @@ def test_hash_valu_summary_and_alu_roofline(tmp_path, monkeypatch):
     assert rec["dispatches"] == 2 and rec["tokens_per_wave"] == 64
     assert rec["valu_insts_per_wave"] == 589 and rec["salu_insts_per_wave"] == 18
     # 1024 SIMDs issue one VALU instruction every 4 cycles at 2.4 GHz
-    roof = bench.hash_valu_roofline(30e9)
-    want_peak = 1024 * 2.4e9 / 4 * 64 / 589
-    assert roof["bound"] == "alu" and abs(roof["peak"] - want_peak) < 1
-    assert abs(roof["frac"] - 30e9 / want_peak) < 1e-12
+    note = bench.hash_valu_note(30e9)
+    want = 1024 * 2.4e9 / 4 * 64 / 589
+    assert abs(note["tokens_per_s_at_valu_issue_rate"] - want) < 1
+    assert abs(note["frac"] - 30e9 / want) < 1e-12
     saved = json.load(open(tmp_path / "valu_hash_b1024s4096.json"))
     saved["hash_source_sha256_16"] = "0" * 16
     json.dump(saved, open(tmp_path / "valu_hash_b1024s4096.json", "w"))
-    assert bench.hash_valu_roofline(30e9) is None
+    assert bench.hash_valu_note(30e9) is None
 
 
 def test_memory_read_traffic_splits_hash_and_gather(tmp_path, monkeypatch):
@@ -130,3 +130,38 @@ def test_memory_read_traffic_splits_hash_and_gather(tmp_path, monkeypatch):
     json.dump(saved, open(tmp_path / bench.MEMORY_READ_TRAFFIC, "w"))
     assert bench.memory_read_bytes("gather") is None
     assert bench.memory_read_bytes("hash") == rec["hash"]["bytes_per_launch"]
+
+
+def test_host_cpu_share_counts_usable_cpus():
+    share = bench.host_cpu_share()
+    assert 1 <= share["threads"] <= share["affinity_cpus"] <= share["host_cpus"]
+    if share["cgroup_cpu_quota"] is not None:
+        assert share["threads"] <= max(1, int(share["cgroup_cpu_quota"]))
+
+
+def test_footprint_summary_attributes_dispatches(tmp_path, monkeypatch):
+    H = 7168
+    n = bench.FOOTPRINT_COUNTER_LAUNCHES
+    fields = ["Dispatch_Id", "Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value"]
+    cp = "(anonymous namespace)::copy_probe_kernel(unsigned int __vector(4) const*, long)"
+    bk = "void (anonymous namespace)::gate_bwd_kernel<7, 2, true, 3, true>(long)"
+    pk = "void (anonymous namespace)::stream_probe_kernel<4, 3>(long)"
+    copy_bytes = 2 * 32768 * H
+    for counter, scale in (("FETCH_SIZE", 2.0), ("WRITE_SIZE", 1.0)):
+        rows = [(cp, copy_bytes / scale / 1024)]
+        for T in bench.FOOTPRINT_COUNTER_TOKENS:
+            part = (8 if counter == "FETCH_SIZE" else 6) * T * H
+            rows += [(bk, part / scale / 1024)] * n + [(pk, 1.1 * part / scale / 1024)] * n
+        with open(tmp_path / f"{counter}.csv", "w", newline="") as f:
+            w = csv.DictWriter(f, fieldnames=fields)
+            w.writeheader()
+            for i, (name, value) in enumerate(rows):
+                w.writerow({"Dispatch_Id": i, "Kernel_Name": name, "Grid_Size": 1,
+                            "Counter_Name": counter, "Counter_Value": value})
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    rec = bench.footprint_from_counters([str(tmp_path / "FETCH_SIZE.csv"),
+                                         str(tmp_path / "WRITE_SIZE.csv")])
+    for T in bench.FOOTPRINT_COUNTER_TOKENS:
+        d = rec["per_tokens"][str(T)]
+        assert abs(d["gate_bwd_kernel"]["measured_over_algorithmic"] - 1.0) < 1e-12
+        assert abs(d["stream_probe_kernel"]["measured_over_algorithmic"] - 1.1) < 1e-12

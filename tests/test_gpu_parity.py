@@ -53,19 +53,43 @@ def to_host_bits(t):
     return t.view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-def run_gpu(eg, d, dev, backward=True):
-    """Forward (+ backward + reduction) on the GPU; returns host arrays."""
+def same_bits(a, b):
+    import torch
+    view = torch.int16 if a.dtype == torch.bfloat16 else torch.int32
+    return torch.equal(a.view(view), b.view(view))
+
+
+def run_gpu(eg, d, dev, backward=True, rerun=False):
+    """Forward (+ backward + reduction) on the GPU; returns host arrays. With
+    `rerun`, every call runs a second time into fresh outputs, and each
+    output must equal the first run's bit for bit."""
     import torch
     T, H = d["x"].shape
     x, k, v = to_dev(d["x"], dev), to_dev(d["k"], dev), to_dev(d["v"], dev)
     wh = torch.from_numpy(d["wh"]).to(dev)
     we = torch.from_numpy(d["we"]).to(dev)
     out, gate = eg.tk_engram_gate_fwd(x, k, v, wh, we)
+    if rerun:
+        out2, gate2 = eg.tk_engram_gate_fwd(x, k, v, wh, we)
+        torch.cuda.synchronize()
+        assert same_bits(out, out2) and same_bits(gate, gate2), "forward rerun differs"
+        del out2, gate2
     res = {}
     if backward:
         g = to_dev(d["grad_out"], dev)
         dx, dk, dv, ws, P = eg.tk_engram_gate_bwd(g, x, k, v, wh, we)
         dwh, dwe = eg.tk_engram_grad_w_reduce(ws, P, H, wh, we)
+        if rerun:
+            again = eg.tk_engram_gate_bwd(g, x, k, v, wh, we)
+            again_w = eg.tk_engram_grad_w_reduce(again[3], P, H, wh, we)
+            torch.cuda.synchronize()
+            for name, a, b in (("dx", dx, again[0]), ("dk", dk, again[1]), ("dv", dv, again[2]),
+                               ("partials", ws, again[3]), ("dwh", dwh, again_w[0]),
+                               ("dwe", dwe, again_w[1])):
+                assert same_bits(a, b), f"backward rerun differs in {name}"
+            say(f"  rerun bit-identical (T={T} H={H}): out, gate, dx, dk, dv, partials, "
+                "dwh, dwe")
+            del again, again_w
         torch.cuda.synchronize()
         del g
         res.update(dx=to_host_bits(dx), dk=to_host_bits(dk), dv=to_host_bits(dv),
@@ -185,7 +209,7 @@ def test_full_size(eg, cuda_device, cfg):
     c = synth.CONFIGS[cfg]
     say(f"[config {cfg}] {c.name}: generating T={c.T} H={c.H}")
     d = synth.make_inputs(cfg)
-    g = run_gpu(eg, d, cuda_device)
+    g = run_gpu(eg, d, cuda_device, rerun=True)
     say(f"[config {cfg}] GPU done (P={g['P']}), comparing with the oracle")
     assert_report(compare(d, g), name=c.name)
     assert_dv_is_gate_times_grad(d, g)

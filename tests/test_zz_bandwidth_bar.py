@@ -1,9 +1,11 @@
 """The bandwidth bar: on the H=4096 and H=7168 workloads (16384 and 32768
-tokens), the forward and the backward kernel each sustain at least 70% of
-MI355X's 8 TB/s in algorithmic bytes. Collected last, so that a slow box
+tokens) and on the ragged stress workload at H=7168 (65537 tokens), the
+forward and the backward each sustain at least 70% of MI355X's 8 TB/s in
+algorithmic bytes, the backward's time being the backward kernel and the
+weight-gradient reduction together. Collected late, so that a slow box
 cannot hide a correctness failure behind it; each figure is the best of
-five averages over 20 back-to-back launches, to keep box-to-box noise (about
-2%) out of the verdict."""
+five averages over 20 back-to-back launches (of the pair, for the
+backward), to keep box-to-box noise (about 2%) out of the verdict."""
 
 import os
 import sys
@@ -27,11 +29,15 @@ def test_forward_and_backward_reach_70_percent_of_hbm(cuda_device, cfg):
     w = bench.Workload(cfg, cuda_device, eg)
     ab = bench.algorithmic_bytes(w.T, w.H)
     fwd_us = min(bench.avg_launch_us(w.fwd, 20) for _ in range(5))
-    bwd_us = min(bench.avg_launch_us(w.bwd, 20) for _ in range(5))
+    def bwd_and_reduce():
+        w.bwd()
+        w.red()
+
+    bwd_us = min(bench.avg_launch_us(bwd_and_reduce, 20) for _ in range(5))
     w.free()
     torch.cuda.empty_cache()
     f = ab["fwd"] / (fwd_us * 1e3) / bench.HBM_PEAK_GBPS
     b = ab["bwd"] / (bwd_us * 1e3) / bench.HBM_PEAK_GBPS
     print(f"[bandwidth bar T={w.T} H={w.H}] fwd {fwd_us:.1f} us {f:.3f}, "
-          f"bwd {bwd_us:.1f} us {b:.3f} of 8 TB/s", flush=True)
+          f"bwd + reduce {bwd_us:.1f} us {b:.3f} of 8 TB/s", flush=True)
     assert f >= BAR and b >= BAR, (f, b)
