@@ -24,6 +24,7 @@ from ._binding import (  # noqa: F401
     tk_engram_bwd_workspace_bytes,
     tk_engram_copy_probe,
     tk_engram_gate_bwd,
+    tk_engram_gate_bwd_reduce_noalloc,
     tk_engram_gate_fwd,
     tk_engram_grad_w_reduce,
     tk_engram_fused_weight,

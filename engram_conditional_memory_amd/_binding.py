@@ -31,6 +31,7 @@ EXPORTS = (
     "tk_engram_num_partials", "tk_engram_bwd_workspace_bytes",
     "tk_engram_copy_probe", "tk_status_string", "tk_abi_version", "tk_engram_hash",
     "tk_engram_gather", "tk_engram_fused_weight", "tk_engram_stream_probe",
+    "tk_engram_gate_bwd_reduce_noalloc",
 )
 
 HASH_MAX_NGRAM = 4
@@ -64,6 +65,8 @@ def load_library(path: str = LIB) -> ctypes.CDLL:
     L.tk_engram_gate_bwd.restype = i32
     L.tk_engram_grad_w_reduce.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp]
     L.tk_engram_grad_w_reduce.restype = i32
+    L.tk_engram_gate_bwd_reduce_noalloc.argtypes = [vp] * 11 + [i64, i64, dbl, dbl, vp]
+    L.tk_engram_gate_bwd_reduce_noalloc.restype = i32
     L.tk_engram_num_partials.argtypes = [i64, i64]
     L.tk_engram_num_partials.restype = i64
     L.tk_engram_bwd_workspace_bytes.argtypes = [i64, i64]
@@ -211,6 +214,32 @@ def tk_engram_grad_w_reduce(workspace, P, H, wh, we, dwh=None, dwe=None, stream=
         _need(dwe, "dwe", f32, (H,), dev), _stream_handle(dev, stream))
     _check("tk_engram_grad_w_reduce", st)
     return dwh, dwe
+
+
+def tk_engram_gate_bwd_reduce_noalloc(grad_out, x, k, v, wh, we, dx=None, dk=None, dv=None,
+                                      dwh=None, dwe=None, eps=EPS, dsqrt_clamp=DSQRT_CLAMP,
+                                      stream=None):
+    """dx, dk, dv (bf16 [T, H]) and dwh, dwe (fp32 [H]) in one call whose
+    weight-gradient partials stay in the library's own device memory; the
+    C call allocates nothing (outputs left as None are allocated here)."""
+    torch = _torch()
+    T, H, dev = _rows(x)
+    bf, f32 = torch.bfloat16, torch.float32
+    dx = torch.empty((T, H), dtype=bf, device=dev) if dx is None else dx
+    dk = torch.empty((T, H), dtype=bf, device=dev) if dk is None else dk
+    dv = torch.empty((T, H), dtype=bf, device=dev) if dv is None else dv
+    dwh = torch.empty((H,), dtype=f32, device=dev) if dwh is None else dwh
+    dwe = torch.empty((H,), dtype=f32, device=dev) if dwe is None else dwe
+    args = [_need(grad_out, "grad_out", bf, (T, H), dev), _need(x, "x", bf, (T, H), dev),
+            _need(k, "k", bf, (T, H), dev), _need(v, "v", bf, (T, H), dev),
+            _need(wh, "wh", f32, (H,), dev), _need(we, "we", f32, (H,), dev),
+            _need(dx, "dx", bf, (T, H), dev), _need(dk, "dk", bf, (T, H), dev),
+            _need(dv, "dv", bf, (T, H), dev), _need(dwh, "dwh", f32, (H,), dev),
+            _need(dwe, "dwe", f32, (H,), dev)]
+    st = load_library().tk_engram_gate_bwd_reduce_noalloc(
+        *args, T, H, float(eps), float(dsqrt_clamp), _stream_handle(dev, stream))
+    _check("tk_engram_gate_bwd_reduce_noalloc", st)
+    return dx, dk, dv, dwh, dwe
 
 
 def _probe_tensors(tensors):

@@ -44,8 +44,12 @@
 #include <cmath>
 #include <cstddef>
 #include <cstdint>
+#include <mutex>
 
 #include "tk_engram.h"
+
+// Device memory of tk_engram_gate_bwd_reduce_noalloc (see scratch_of below).
+static __device__ __align__(256) float scratch[TK_ENGRAM_NOALLOC_SCRATCH_BYTES / sizeof(float)];
 
 namespace {
 
@@ -923,6 +927,41 @@ tk_status enqueue_reduce(const float* workspace, int64_t P, int64_t H, const flo
   return launch(grad_w_reduce_kernel, grid, kRedCols4 * kRedSlices, args, st);
 }
 
+// ---- library-owned partials ---------------------------------------------------
+
+// The weight-gradient partials of tk_engram_gate_bwd_reduce_noalloc live in
+// this array: enough for every legal (T, H), P * H <= 256 * 8192 floats
+// (8 MiB). Each GPU the library runs on holds its own copy until the process
+// ends. In host code `scratch` names a host-side stand-in, not the device
+// copy, so kernels are given the device address from hipGetSymbolAddress,
+// looked up once per device with that device current and kept below.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+float* g_scratch[kMaxDevices];
+
+tk_status scratch_of(hipStream_t stream, float** out) {
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return TK_ERR_LAUNCH;
+  int dev = cur;
+  if (stream) {
+    hipDevice_t sd;
+    if (hipStreamGetDevice(stream, &sd) != hipSuccess) return TK_ERR_LAUNCH;
+    dev = (int)sd;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return TK_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch[dev]) {
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return TK_ERR_LAUNCH;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur && hipSetDevice(cur) != hipSuccess) return TK_ERR_LAUNCH;
+    if (e != hipSuccess || p == nullptr) return TK_ERR_LAUNCH;
+    g_scratch[dev] = static_cast<float*>(p);
+  }
+  *out = g_scratch[dev];
+  return TK_SUCCESS;
+}
+
 }  // namespace
 
 extern "C" {
@@ -996,6 +1035,28 @@ tk_status tk_engram_grad_w_reduce(const float* workspace, int64_t P, int64_t H,
     return TK_ERR_ALIGN;
   return enqueue_reduce(workspace, P, H, wh, we, dwh, dwe,
                         reinterpret_cast<hipStream_t>(stream));
+}
+
+tk_status tk_engram_gate_bwd_reduce_noalloc(const uint16_t* grad_out, const uint16_t* x,
+                                            const uint16_t* k, const uint16_t* v,
+                                            const float* wh, const float* we, uint16_t* dx,
+                                            uint16_t* dk, uint16_t* dv, float* dwh,
+                                            float* dwe, int64_t T, int64_t H, double eps,
+                                            double dsqrt_clamp, void* stream) {
+  tk_status st = check_bwd_args(grad_out, x, k, v, wh, we, dx, dk, dv, T, H, eps, dsqrt_clamp);
+  if (st != TK_SUCCESS) return st;
+  if (!dwh || !dwe) return TK_ERR_NULL;
+  if (!aligned16(dwh) || !aligned16(dwe)) return TK_ERR_ALIGN;
+  if (tk_engram_bwd_workspace_bytes(T, H) > sizeof(scratch)) return TK_ERR_WORKSPACE;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  float* partial = nullptr;
+  st = scratch_of(hs, &partial);
+  if (st != TK_SUCCESS) return st;
+  if (T > 0) {
+    st = enqueue_bwd(grad_out, x, k, v, wh, we, dx, dk, dv, partial, T, H, eps, dsqrt_clamp, hs);
+    if (st != TK_SUCCESS) return st;
+  }
+  return enqueue_reduce(partial, tk_engram_num_partials(T, H), H, wh, we, dwh, dwe, hs);
 }
 
 tk_status tk_engram_fused_weight(const float* wh, const float* we, double* w, int64_t H,

@@ -25,10 +25,12 @@
  *   - All tensor pointers are DEVICE pointers owned by the caller; the hash,
  *     the gather and the stream probe also take small HOST arrays (of
  *     parameters or of device pointers), read before the call returns, as
- *     stated with each call. The library never
- *     allocates, frees or synchronises; each call only enqueues work on
- *     `stream` (a hipStream_t passed as void*, NULL = default stream) and
- *     returns. Outputs are overwritten, never accumulated into.
+ *     stated with each call. No call allocates, frees or synchronises;
+ *     each call only enqueues work on `stream` (a hipStream_t passed as
+ *     void*, NULL = default stream) and returns. Outputs are overwritten,
+ *     never accumulated into. The one piece of library-owned device memory
+ *     is the static array of tk_engram_gate_bwd_reduce_noalloc, which the
+ *     HIP runtime places on each GPU with the library's code.
  *   - Inputs and outputs must not overlap (undefined behaviour otherwise).
  *   - Arithmetic: every row sum (squares, the weighted dot product
  *     sum_i x_i k_i wh_i we_i, and sum_i grad_out_i v_i) is accumulated in
@@ -156,6 +158,38 @@ tk_status tk_engram_gate_bwd(const uint16_t* grad_out, const uint16_t* x,
 tk_status tk_engram_grad_w_reduce(const float* workspace, int64_t P, int64_t H,
                                   const float* wh, const float* we, float* dwh,
                                   float* dwe, void* stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * backward and the weight-gradient reduction in one call, with the
+ * weight-gradient partials kept in library-owned device memory instead of a
+ * caller's workspace. Its results are those of tk_engram_gate_bwd followed
+ * by tk_engram_grad_w_reduce, bit for bit (the same kernels and the same P).
+ *
+ *   grad_out, x, k, v, wh, we, dx, dk, dv, eps, dsqrt_clamp : as for
+ *                     tk_engram_gate_bwd
+ *   dwh, dwe        : fp32 [H], as for tk_engram_grad_w_reduce
+ *
+ * The partials live in a static device array of
+ * TK_ENGRAM_NOALLOC_SCRATCH_BYTES (8 MiB), enough for every (T, H) the gate
+ * calls accept; a shape needing more returns TK_ERR_WORKSPACE. Each GPU the
+ * library runs on holds its own copy until the process ends; its address is
+ * looked up once per device, on the first call there. The call allocates
+ * nothing and writes no memset. Every call on one GPU shares that GPU's
+ * array, which keeps the last call's partials: the backward writes every
+ * partial it uses, so nothing needs clearing, but calls that overlap on one
+ * GPU (two streams in flight at once) race and must be serialised by the
+ * caller. T = 0 writes zeros to dwh and dwe.
+ */
+#define TK_ENGRAM_NOALLOC_SCRATCH_BYTES (256u * 8192u * 4u)
+
+tk_status tk_engram_gate_bwd_reduce_noalloc(const uint16_t* grad_out, const uint16_t* x,
+                                            const uint16_t* k, const uint16_t* v,
+                                            const float* wh, const float* we, uint16_t* dx,
+                                            uint16_t* dk, uint16_t* dv, float* dwh,
+                                            float* dwe, int64_t T, int64_t H, double eps,
+                                            double dsqrt_clamp, void* stream);
 
 /*
  * Fused RMSNorm weight (section "5. Engram": engram_fused_weight, the weight

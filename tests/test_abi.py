@@ -85,6 +85,15 @@ def red(**kw):
         a["ws"], a["P"], a["H"], a["wh"], a["we"], a["dwh"], a["dwe"], None)
 
 
+def noalloc(**kw):
+    a = dict(g=A16, x=A16, k=A16, v=A16, wh=A16, we=A16, dx=A16, dk=A16, dv=A16,
+             dwh=A16, dwe=A16, T=4, H=64, eps=1e-6, clamp=1e-4)
+    a.update(kw)
+    return eg.load_library().tk_engram_gate_bwd_reduce_noalloc(
+        a["g"], a["x"], a["k"], a["v"], a["wh"], a["we"], a["dx"], a["dk"], a["dv"],
+        a["dwh"], a["dwe"], a["T"], a["H"], a["eps"], a["clamp"], None)
+
+
 def test_forward_argument_checks():
     assert fwd(T=-1) == B.TK_ERR_SHAPE
     assert fwd(H=0) == B.TK_ERR_SHAPE
@@ -116,6 +125,21 @@ def test_backward_argument_checks():
     for clamp in (1e-300, 1e-39, 1e-45, 1e39, -1e-4, float("nan")):
         assert bwd(clamp=clamp) == B.TK_ERR_VALUE, clamp
         assert bwd(clamp=clamp, T=0, ws=None, wsb=0) == B.TK_ERR_VALUE, clamp
+
+
+def test_noalloc_backward_argument_checks():
+    # only failing checks here: a call that passed them would launch
+    assert noalloc(T=-3) == B.TK_ERR_SHAPE
+    assert noalloc(H=20) == B.TK_ERR_ALIGN
+    assert noalloc(H=16384) == B.TK_ERR_UNSUPPORTED
+    assert noalloc(eps=-1.0) == B.TK_ERR_VALUE
+    for clamp in (0.0, 1e-39, float("inf")):
+        assert noalloc(clamp=clamp) == B.TK_ERR_VALUE, clamp
+    for name in ("g", "x", "k", "v", "wh", "we", "dx", "dk", "dv", "dwh", "dwe"):
+        assert noalloc(**{name: None}) == B.TK_ERR_NULL, name
+        assert noalloc(**{name: A4}) == B.TK_ERR_ALIGN, name
+    assert noalloc(T=0, dwh=None) == B.TK_ERR_NULL
+    assert noalloc(T=0, dwe=A4) == B.TK_ERR_ALIGN
 
 
 def test_reduce_argument_checks():
@@ -153,6 +177,14 @@ def test_probe_bindings_refuse_host_tensors():
         eg.tk_engram_copy_probe(a, b)
     with pytest.raises(ValueError, match="GPU"):
         eg.tk_engram_stream_probe([a], [b])
+
+
+def test_noalloc_binding_refuses_host_tensors():
+    import torch
+    x = torch.zeros(4, 64, dtype=torch.bfloat16)
+    w = torch.ones(64)
+    with pytest.raises(ValueError):
+        eg.tk_engram_gate_bwd_reduce_noalloc(x, x, x, x, w, w)
 
 
 def test_missing_library_raises(tmp_path):
