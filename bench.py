@@ -457,15 +457,18 @@ def footprint_counter_run(eg, dev, H: int = 7168) -> dict:
     return out
 
 
-def footprint_from_counters(csvs: list, H: int = 7168) -> dict:
-    """Per token count, the mean per dispatch of every counter in the given
-    rocprofv3 --pmc runs of --footprint-counters, for the backward kernel and
-    the stream probe; FETCH_SIZE and WRITE_SIZE also as bytes (scaled by
-    their reading for the copy probe) over the algorithmic bytes. Written to
-    profiles/footprint_counters_h<H>.json."""
+def footprint_from_counters(csvs: list, H: int = 7168, name: str = "") -> dict:
+    """Per token count, the mean per call of every counter in the given
+    rocprofv3 --pmc runs of --footprint-counters (summed over a backward
+    call's epoch launches), for the backward kernel and the stream probe;
+    FETCH_SIZE and WRITE_SIZE also as bytes (scaled by their reading for the
+    copy probe) over the algorithmic bytes. Written to
+    profiles/footprint_counters_h<H><name>.json."""
     import csv
     n = FOOTPRINT_COUNTER_LAUNCHES
-    rec = {"H": H, "tokens": list(FOOTPRINT_COUNTER_TOKENS), "launches_each": n, "runs": []}
+    per_call = [gate_launches(T, H)["gate_bwd_kernel"] for T in FOOTPRINT_COUNTER_TOKENS]
+    rec = {"H": H, "tokens": list(FOOTPRINT_COUNTER_TOKENS), "calls_each": n, "runs": [],
+           "bwd_launches_per_call": per_call, "kernel_source_sha256_16": kernel_source_hash()}
     table = {}
     for path in csvs:
         names = sorted({r["Counter_Name"] for r in csv.DictReader(open(path))})
@@ -476,16 +479,20 @@ def footprint_from_counters(csvs: list, H: int = 7168) -> dict:
             cp = [v for _, k, _, v in rows if k == "copy_probe_kernel"]
             bw = [v for _, k, _, v in rows if k == "gate_bwd_kernel"]
             pr = [v for _, k, _, v in rows if k == "stream_probe_kernel"]
-            if len(bw) != n * len(FOOTPRINT_COUNTER_TOKENS) or len(pr) != len(bw) or len(cp) != 1:
+            if (len(bw) != n * sum(per_call) or len(pr) != n * len(FOOTPRINT_COUNTER_TOKENS)
+                    or len(cp) != 1):
                 raise SystemExit(f"{path}: unexpected dispatch counts {len(cp)}, {len(bw)}, "
                                  f"{len(pr)} for {counter}")
             scale = None
             if counter in ("FETCH_SIZE", "WRITE_SIZE"):
                 scale = 2 * 32768 * H / (1024.0 * cp[0])
                 rec[f"{counter.lower()}_scale"] = scale
+            starts = np.concatenate([[0], np.cumsum([n * L for L in per_call])])
             for i, T in enumerate(FOOTPRINT_COUNTER_TOKENS):
-                for kern, vals in (("gate_bwd_kernel", bw), ("stream_probe_kernel", pr)):
-                    m = float(np.mean(vals[i * n:(i + 1) * n]))
+                # per call: the backward's epoch launches summed, one probe launch
+                for kern, vals in (("gate_bwd_kernel", bw[starts[i]:starts[i + 1]]),
+                                   ("stream_probe_kernel", pr[i * n:(i + 1) * n])):
+                    m = float(np.sum(vals)) / n
                     d = table.setdefault(str(T), {}).setdefault(kern, {})
                     d[counter] = m
                     if scale is not None:
@@ -501,11 +508,101 @@ def footprint_from_counters(csvs: list, H: int = 7168) -> dict:
                 d["utcl1_miss_per_MiB"] = (d["TCP_UTCL1_TRANSLATION_MISS_sum"]
                                            / (14 * int(T) * H / 2 ** 20))
     rec["per_tokens"] = table
-    path = os.path.join(PROFILES, f"footprint_counters_h{H}.json")
+    path = os.path.join(PROFILES, f"footprint_counters_h{H}{name}.json")
     with open(path, "w") as f:
         json.dump(rec, f, indent=1, sort_keys=True)
         f.write("\n")
     return rec
+
+
+def _kernel_label(name: str) -> str:
+    """`gate_bwd_kernel<7, 2, true, 3, true, false>` from a demangled name."""
+    name = name.replace("(anonymous namespace)::", "")
+    if name.startswith("void "):
+        name = name[len("void "):]
+    return name.split("(")[0].strip()
+
+
+TRACE_DOC = """bench.py defaults: 50 timed steps after 20 warm-up steps, then each call alone
+50 times back to back (plus one untimed call), on T=32768 H=7168; then 23
+steps (3 warm-up) of the autograd module on the same tensors (it runs the
+fused-weight forms of the gate kernels, the last template argument `true`);
+the same calls on T=16384 H=4096 after at least 50 ms of warm-up steps; 20
+steps and 20 single calls on the stress workload (T=65537, H=7168) after at
+least 50 ms of warm-up; the 1024-token forward 51 times hot and 50 times after
+a 1 GiB write; the copy probe; the stream probe for the 3-in/1-out and
+4-in/3-out mixes; the N-gram hash; the table gather on uniform, then Zipf(1)
+token ids; the fused weight at H=7168; a 1024-token step at H=4096 eagerly,
+on the capture stream and replayed from a HIP graph."""
+
+
+def trace_summary(trace_csv: str, stats_csv: str, cmd: str) -> str:
+    """Markdown summary of a rocprofv3 kernel trace of the default bench run:
+    rocprofv3's per-dispatch statistics of the library's kernels, then the
+    gate kernels per call on each H = 7168 workload (a call on a long batch
+    is several epoch launches, summed here; `span` also counts the gaps
+    between them, as HIP events around the call do)."""
+    import csv
+    rows = sorted(csv.DictReader(open(trace_csv)), key=lambda r: int(r["Start_Timestamp"]))
+    out = ["# Engram kernels, bench.py default run: rocprofv3 kernel trace", "",
+           "Command (from the repository root, on one MI355X):", "", "    " + cmd, "",
+           f"Summarised by `python3 bench.py --trace-from {os.path.basename(trace_csv)} "
+           f"{os.path.basename(stats_csv)}` (paths of the run's output directory).", "",
+           TRACE_DOC, "", f"Kernel source sha256 prefix: {kernel_source_hash()}.", "",
+           "Per dispatch, from the stats file (durations in microseconds):", "",
+           "| kernel | dispatches | average | min | max | % of GPU time |",
+           "|---|---|---|---|---|---|"]
+    for r in csv.DictReader(open(stats_csv)):
+        lab = _kernel_label(r["Name"])
+        if not lab.split("<")[0].endswith(("_kernel", "_kernel_vec", "_kernel_any")):
+            continue
+        if lab.startswith(("at::", "void at::")):
+            continue
+        out.append(f"| `{lab}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                   f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                   f"{float(r['Percentage']):.2f} |")
+    # the H = 7168 gate kernels in time order: the main workload's unfused
+    # kernels come before the autograd module's fused ones, the stress
+    # workload's after them
+    fused = [int(r["Start_Timestamp"]) for r in rows
+             if _kernel_label(r["Kernel_Name"]).startswith("gate_")
+             and _kernel_label(r["Kernel_Name"]).endswith(", true>")
+             and "<7, 2" in r["Kernel_Name"]]
+    t_fused = min(fused) if fused else None
+    out += ["", "Per call of the gate kernels at H = 7168 (microseconds; `kernel` sums a "
+            "call's epoch launches, `span` runs from the first launch's start to the last "
+            "one's end):", "",
+            "| workload | kernel | launches per call | calls | kernel average | span average |",
+            "|---|---|---|---|---|---|"]
+    for wl, T, when in (("T=32768, H=7168 (main)", 32768, "before"),
+                        ("T=32768, H=7168 (autograd module)", 32768, "fused"),
+                        ("T=65537, H=7168 (stress)", 65537, "after")):
+        L = gate_launches(T, 7168)
+        for kern in ("gate_fwd_kernel", "gate_bwd_kernel"):
+            sel = []
+            for r in rows:
+                lab = _kernel_label(r["Kernel_Name"])
+                if not lab.startswith(kern + "<7, 2"):
+                    continue
+                st = int(r["Start_Timestamp"])
+                is_fused = lab.endswith(", true>")
+                if when == "fused" and not is_fused:
+                    continue
+                if when != "fused" and (is_fused or t_fused is None
+                                        or (st > t_fused) != (when == "after")):
+                    continue
+                sel.append((st, int(r["End_Timestamp"]), lab))
+            n = L[kern]
+            if not sel or len(sel) % n:
+                out.append(f"| {wl} | `{kern}` | {n} | (dispatch count {len(sel)} "
+                           "not a multiple) | | |")
+                continue
+            calls = [sel[i:i + n] for i in range(0, len(sel), n)]
+            k_us = np.mean([sum(e - b for b, e, _ in c) for c in calls]) / 1e3
+            s_us = np.mean([c[-1][1] - c[0][0] for c in calls]) / 1e3
+            out.append(f"| {wl} | `{sel[0][2]}` | {n} | {len(calls)} | {k_us:.2f} | "
+                       f"{s_us:.2f} |")
+    return "\n".join(out) + "\n"
 
 
 def time_graph_step(eg, dev, T: int = 1024, H: int = 4096, reps: int = 50) -> dict:
@@ -820,11 +917,27 @@ def read_counter_csv(path: str, counter: str) -> dict:
     return {k: float(np.mean(v)) for k, v in per.items()}
 
 
+def gate_launches(T: int, H: int) -> dict:
+    """Kernel launches per call of the forward and the backward at (T, H):
+    both walk their rows in epochs (tk_engram_gate_launches)."""
+    import engram_conditional_memory_amd as eg
+    return {"gate_fwd_kernel": eg.tk_engram_gate_launches(T, H, False),
+            "gate_bwd_kernel": eg.tk_engram_gate_launches(T, H, True)}
+
+
 def traffic_from_counters(fetch_csv: str, write_csv: str, workload: int) -> dict:
+    """HBM bytes per call of each kernel: the mean per dispatch times the
+    kernel's launches per call (several for the gate kernels on long
+    batches, one for the rest)."""
     import synth
     c = synth.CONFIGS[workload]
     fetch = read_counter_csv(fetch_csv, "FETCH_SIZE")
     write = read_counter_csv(write_csv, "WRITE_SIZE")
+    per_call = gate_launches(c.T, c.H)
+    for counts in (fetch, write):
+        for k, n in per_call.items():
+            if k in counts:
+                counts[k] *= n
     copy_bytes = 2 * c.T * c.H              # the copy probe reads and writes this
     f_scale = copy_bytes / (1024.0 * fetch["copy_probe_kernel"])
     w_scale = copy_bytes / (1024.0 * write["copy_probe_kernel"])
@@ -834,11 +947,11 @@ def traffic_from_counters(fetch_csv: str, write_csv: str, workload: int) -> dict
     for k in sorted(set(fetch) & set(write)):
         rd = fetch[k] * 1024.0 * f_scale
         wr = write[k] * 1024.0 * w_scale
-        kernels[k] = {"fetch_kib_per_dispatch": fetch[k], "write_kib_per_dispatch": write[k],
+        kernels[k] = {"fetch_kib_per_call": fetch[k], "write_kib_per_call": write[k],
                       "read_bytes": rd, "write_bytes": wr, "bytes_per_launch": rd + wr,
                       "algorithmic_bytes": algo.get(k),
                       "measured_over_algorithmic": (rd + wr) / algo[k] if k in algo else None}
-    rec = {"workload": c.name, "T": c.T, "H": c.H,
+    rec = {"workload": c.name, "T": c.T, "H": c.H, "launches_per_call": per_call,
            "kernel_source_sha256_16": kernel_source_hash(),
            "calibration": {"copy_bytes_each_way": copy_bytes,
                            "fetch_scale": f_scale, "write_scale": w_scale},
@@ -1006,8 +1119,13 @@ def main():
                          + " (H = 7168), for rocprofv3 --pmc runs")
     ap.add_argument("--footprint-from", nargs="+", metavar="CSV",
                     help="summarise rocprofv3 --pmc runs of --footprint-counters")
+    ap.add_argument("--footprint-name", default="",
+                    help="suffix of the --footprint-from record's file name")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="summarise two rocprofv3 --pmc runs instead of benchmarking")
+    ap.add_argument("--trace-from", nargs=2, metavar=("TRACE_CSV", "STATS_CSV"),
+                    help="summarise a rocprofv3 --kernel-trace --stats run of the default "
+                         "bench into profiles/engram_kernels_bench_default_kernel_trace.md")
     ap.add_argument("--memory-read-traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="summarise two rocprofv3 --pmc runs over --memory-read (the hash's "
                          "and the gather's HBM bytes per launch)")
@@ -1019,8 +1137,17 @@ def main():
         rec = memory_read_traffic(*args.memory_read_traffic_from)
         print(json.dumps(rec, indent=1, sort_keys=True))
         return
+    if args.trace_from:
+        cmd = ("rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof -o bench "
+               "-- python3 bench.py --no-cpu-baseline")
+        text = trace_summary(args.trace_from[0], args.trace_from[1], cmd)
+        with open(os.path.join(PROFILES, "engram_kernels_bench_default_kernel_trace.md"), "w") as f:
+            f.write(text)
+        print(text)
+        return
     if args.footprint_from:
-        print(json.dumps(footprint_from_counters(args.footprint_from), indent=1, sort_keys=True))
+        print(json.dumps(footprint_from_counters(args.footprint_from, name=args.footprint_name),
+                         indent=1, sort_keys=True))
         return
     if args.valu_from:
         print(json.dumps(valu_from_counters(args.valu_from), indent=1, sort_keys=True))

@@ -24,8 +24,11 @@ from ._binding import (  # noqa: F401
     tk_engram_bwd_workspace_bytes,
     tk_engram_copy_probe,
     tk_engram_gate_bwd,
+    tk_engram_gate_bwd_fused,
     tk_engram_gate_bwd_reduce_noalloc,
     tk_engram_gate_fwd,
+    tk_engram_gate_fwd_fused,
+    tk_engram_gate_launches,
     tk_engram_grad_w_reduce,
     tk_engram_fused_weight,
     tk_engram_gather,

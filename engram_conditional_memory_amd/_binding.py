@@ -31,7 +31,8 @@ EXPORTS = (
     "tk_engram_num_partials", "tk_engram_bwd_workspace_bytes",
     "tk_engram_copy_probe", "tk_status_string", "tk_abi_version", "tk_engram_hash",
     "tk_engram_gather", "tk_engram_fused_weight", "tk_engram_stream_probe",
-    "tk_engram_gate_bwd_reduce_noalloc",
+    "tk_engram_gate_bwd_reduce_noalloc", "tk_engram_gate_fwd_fused",
+    "tk_engram_gate_bwd_fused", "tk_engram_gate_launches",
 )
 
 HASH_MAX_NGRAM = 4
@@ -65,10 +66,17 @@ def load_library(path: str = LIB) -> ctypes.CDLL:
     L.tk_engram_gate_bwd.restype = i32
     L.tk_engram_grad_w_reduce.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp]
     L.tk_engram_grad_w_reduce.restype = i32
+    L.tk_engram_gate_fwd_fused.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, dbl, vp]
+    L.tk_engram_gate_fwd_fused.restype = i32
+    L.tk_engram_gate_bwd_fused.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
+                                           i64, i64, dbl, dbl, vp]
+    L.tk_engram_gate_bwd_fused.restype = i32
     L.tk_engram_gate_bwd_reduce_noalloc.argtypes = [vp] * 11 + [i64, i64, dbl, dbl, vp]
     L.tk_engram_gate_bwd_reduce_noalloc.restype = i32
     L.tk_engram_num_partials.argtypes = [i64, i64]
     L.tk_engram_num_partials.restype = i64
+    L.tk_engram_gate_launches.argtypes = [i64, i64, i32]
+    L.tk_engram_gate_launches.restype = i64
     L.tk_engram_bwd_workspace_bytes.argtypes = [i64, i64]
     L.tk_engram_bwd_workspace_bytes.restype = sz
     L.tk_engram_copy_probe.argtypes = [vp, vp, sz, vp]
@@ -99,6 +107,10 @@ def tk_abi_version() -> int:
 
 def tk_engram_num_partials(T: int, H: int) -> int:
     return int(load_library().tk_engram_num_partials(T, H))
+
+
+def tk_engram_gate_launches(T: int, H: int, backward: bool) -> int:
+    return int(load_library().tk_engram_gate_launches(T, H, 1 if backward else 0))
 
 
 def tk_engram_bwd_workspace_bytes(T: int, H: int) -> int:
@@ -192,6 +204,48 @@ def tk_engram_gate_bwd(grad_out, x, k, v, wh, we, dx=None, dk=None, dv=None,
                                            float(eps), float(dsqrt_clamp),
                                            _stream_handle(dev, stream))
     _check("tk_engram_gate_bwd", st)
+    return dx, dk, dv, workspace, P
+
+
+def tk_engram_gate_fwd_fused(x, k, v, w, out=None, gate=None, eps=EPS, stream=None):
+    """tk_engram_gate_fwd with the fused weight w = wh * we (fp64 [H])."""
+    torch = _torch()
+    T, H, dev = _rows(x)
+    bf, f32 = torch.bfloat16, torch.float32
+    out = torch.empty((T, H), dtype=bf, device=dev) if out is None else out
+    gate = torch.empty((T,), dtype=f32, device=dev) if gate is None else gate
+    args = [_need(x, "x", bf, (T, H), dev), _need(k, "k", bf, (T, H), dev),
+            _need(v, "v", bf, (T, H), dev), _need(w, "w", torch.float64, (H,), dev),
+            _need(out, "out", bf, (T, H), dev), _need(gate, "gate", f32, (T,), dev)]
+    st = load_library().tk_engram_gate_fwd_fused(*args, T, H, float(eps),
+                                                 _stream_handle(dev, stream))
+    _check("tk_engram_gate_fwd_fused", st)
+    return out, gate
+
+
+def tk_engram_gate_bwd_fused(grad_out, x, k, v, w, dx=None, dk=None, dv=None, workspace=None,
+                             eps=EPS, dsqrt_clamp=DSQRT_CLAMP, stream=None):
+    """tk_engram_gate_bwd with the fused weight w = wh * we (fp64 [H])."""
+    torch = _torch()
+    T, H, dev = _rows(x)
+    bf, f32 = torch.bfloat16, torch.float32
+    P = tk_engram_num_partials(T, H)
+    dx = torch.empty((T, H), dtype=bf, device=dev) if dx is None else dx
+    dk = torch.empty((T, H), dtype=bf, device=dev) if dk is None else dk
+    dv = torch.empty((T, H), dtype=bf, device=dev) if dv is None else dv
+    if workspace is None:
+        workspace = torch.empty((max(P, 1), H), dtype=f32, device=dev)
+    if workspace.dtype != f32 or workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous fp32 GPU tensor")
+    args = [_need(grad_out, "grad_out", bf, (T, H), dev), _need(x, "x", bf, (T, H), dev),
+            _need(k, "k", bf, (T, H), dev), _need(v, "v", bf, (T, H), dev),
+            _need(w, "w", torch.float64, (H,), dev), _need(dx, "dx", bf, (T, H), dev),
+            _need(dk, "dk", bf, (T, H), dev), _need(dv, "dv", bf, (T, H), dev),
+            ctypes.c_void_p(workspace.data_ptr())]
+    st = load_library().tk_engram_gate_bwd_fused(*args, workspace.numel() * 4, T, H,
+                                                 float(eps), float(dsqrt_clamp),
+                                                 _stream_handle(dev, stream))
+    _check("tk_engram_gate_bwd_fused", st)
     return dx, dk, dv, workspace, P
 
 

@@ -2,11 +2,17 @@
 
 The juejin.cn TileKernels page (highlight 5) describes a torch.autograd.Function
 around the Engram gate: forward, backward and the weight-gradient reduction.
-This module is that wrapper over the three C-ABI calls of libtk_engram.so:
+This module is that wrapper over the C-ABI calls of libtk_engram.so:
 
-    forward   tk_engram_gate_fwd        out = x + gate * v
-    backward  tk_engram_gate_bwd        dx, dk, dv and per-block partials
+    forward   tk_engram_fused_weight    w = wh * we (fp64), once per step
+              tk_engram_gate_fwd_fused  out = x + gate * v
+    backward  tk_engram_gate_bwd_fused  dx, dk, dv and per-block partials
               tk_engram_grad_w_reduce   dwh, dwe from the partials
+
+The zhichai.net page's section "5. Engram" lists the fused weight as the
+weight preprocessing ahead of the gate; the forward and the backward read it
+in place of the two RMSNorm weights, and the reduction, which needs the two
+separately, takes wh and we.
 
 The gate itself is the formula of the zhichai.net TileKernels page, section
 "5. Engram". Inputs of any leading shape [..., H] are flattened to [T, H]
@@ -41,8 +47,9 @@ class EngramGateFunction(torch.autograd.Function):
                              f"{tuple(k.shape)}, {tuple(v.shape)}")
         x2, k2, v2 = _rows(x, H), _rows(k, H), _rows(v, H)
         wh_c, we_c = wh.contiguous(), we.contiguous()
-        out, gate = B.tk_engram_gate_fwd(x2, k2, v2, wh_c, we_c, eps=eps)
-        ctx.save_for_backward(x2, k2, v2, wh_c, we_c)
+        w = B.tk_engram_fused_weight(wh_c, we_c)
+        out, gate = B.tk_engram_gate_fwd_fused(x2, k2, v2, w, eps=eps)
+        ctx.save_for_backward(x2, k2, v2, wh_c, we_c, w)
         ctx.eps, ctx.clamp, ctx.lead, ctx.H = eps, dsqrt_clamp, lead, H
         gate = gate.view(lead)
         ctx.mark_non_differentiable(gate)
@@ -50,11 +57,11 @@ class EngramGateFunction(torch.autograd.Function):
 
     @staticmethod
     def backward(ctx, grad_out, grad_gate):
-        x2, k2, v2, wh, we = ctx.saved_tensors
+        x2, k2, v2, wh, we, w = ctx.saved_tensors
         H = ctx.H
         g = _rows(grad_out.to(torch.bfloat16), H)
-        dx, dk, dv, ws, P = B.tk_engram_gate_bwd(g, x2, k2, v2, wh, we, eps=ctx.eps,
-                                                 dsqrt_clamp=ctx.clamp)
+        dx, dk, dv, ws, P = B.tk_engram_gate_bwd_fused(g, x2, k2, v2, w, eps=ctx.eps,
+                                                       dsqrt_clamp=ctx.clamp)
         dwh = dwe = None
         if ctx.needs_input_grad[3] or ctx.needs_input_grad[4]:
             dwh, dwe = B.tk_engram_grad_w_reduce(ws, P, H, wh, we)

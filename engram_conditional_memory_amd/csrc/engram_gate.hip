@@ -43,6 +43,7 @@
 
 #include <cmath>
 #include <cstddef>
+#include <algorithm>
 #include <cstdint>
 #include <mutex>
 
@@ -57,6 +58,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef double f64x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 
@@ -158,28 +160,49 @@ __device__ __forceinline__ void store_chunk(u32x4* __restrict__ p, const u32x4 v
   __builtin_nontemporal_store(v, p);
 }
 
+// The RMSNorm weights as the gate kernels receive them: wh and we (fp32
+// [H]), or their product w = wh * we in fp64 (the fused weight of the
+// "5. Engram" section's weight preprocessing), read as it is (FUSED).
+struct WeightsIn {
+  const f32x4* wh;
+  const f32x4* we;
+  const f64x2* w;
+};
+
 // w_i = wh_i * we_i for the thread's columns, exactly (the product of two
-// fp32 values is exact in fp64). The elementwise backward uses its fp32
-// rounding, (float)w, which is the correctly rounded fp32 product.
-template <int NT, int C, bool FULL>
-__device__ __forceinline__ void load_weights(const f32x4* __restrict__ wh,
-                                             const f32x4* __restrict__ we,
-                                             int tid, int nchunk,
+// fp32 values is exact in fp64), or the fused weight as given. The
+// elementwise backward uses its fp32 rounding, (float)w, which for a product
+// of two fp32 values is the correctly rounded fp32 product.
+template <int NT, int C, bool FULL, bool FUSED>
+__device__ __forceinline__ void load_weights(const WeightsIn& in, int tid, int nchunk,
                                              double (&w64)[C][8]) {
 #pragma unroll
   for (int j = 0; j < C; ++j) {
     const int c = j * NT + tid;
-    f32x4 a0 = {0, 0, 0, 0}, a1 = a0, b0 = a0, b1 = a0;
-    if (FULL || c < nchunk) {
-      a0 = wh[2 * c];
-      a1 = wh[2 * c + 1];
-      b0 = we[2 * c];
-      b1 = we[2 * c + 1];
-    }
+    if constexpr (FUSED) {
+      f64x2 q[4] = {{0.0, 0.0}, {0.0, 0.0}, {0.0, 0.0}, {0.0, 0.0}};
+      if (FULL || c < nchunk) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      w64[j][e] = (double)a0[e] * (double)b0[e];
-      w64[j][e + 4] = (double)a1[e] * (double)b1[e];
+        for (int u = 0; u < 4; ++u) q[u] = in.w[4 * c + u];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        w64[j][2 * u] = q[u][0];
+        w64[j][2 * u + 1] = q[u][1];
+      }
+    } else {
+      f32x4 a0 = {0, 0, 0, 0}, a1 = a0, b0 = a0, b1 = a0;
+      if (FULL || c < nchunk) {
+        a0 = in.wh[2 * c];
+        a1 = in.wh[2 * c + 1];
+        b0 = in.we[2 * c];
+        b1 = in.we[2 * c + 1];
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        w64[j][e] = (double)a0[e] * (double)b0[e];
+        w64[j][e + 4] = (double)a1[e] * (double)b1[e];
+      }
     }
   }
 }
@@ -260,21 +283,26 @@ __device__ __forceinline__ RowScalars row_gate(double sum_xx, double sum_kk,
 // rewritten two rows later, after every thread has passed the barrier of
 // the row in between, so one barrier per row suffices.
 
-// Which rows a workgroup walks: block b takes rows
-//   b * block_stride + i * row_step,  i = 0 .. rows_of(first) - 1,
-// never beyond T and at most `per_block` of them. Contiguous blocks are
-// (block_stride = rows per block, row_step = 1); interleaved blocks are
-// (block_stride = 1, row_step = number of blocks), which keeps the rows in
-// flight across the chip inside one sliding window of the tensors.
+// Which rows a workgroup walks. With G workgroups, block b owns rows
+// b, b + G, b + 2G, ... (row t belongs to block t mod G), which keeps the rows
+// in flight across the chip inside one sliding window of the tensors. A
+// launch covers iterations [iter0, iter0 + iters) of that walk: block b takes
+// rows b + (iter0 + i) G, i = 0 .. rows_of(b) - 1, never beyond T. A long
+// walk is split into several such launches (epochs): the blocks drift apart
+// as they go, widening the window of rows in flight, and each launch boundary
+// brings them back together.
 struct RowWalk {
   int64_t T;
-  int64_t block_stride;
-  int64_t row_step;
-  int64_t per_block;
+  int64_t row_step;  // G
+  int64_t iter0;
+  int64_t iters;
+  __device__ __forceinline__ int64_t first_row(int64_t blk) const {
+    return blk + iter0 * row_step;
+  }
   __device__ __forceinline__ int64_t rows_of(int64_t first) const {
     if (first >= T) return 0;
     const int64_t n = (T - first + row_step - 1) / row_step;
-    return n < per_block ? n : per_block;
+    return n < iters ? n : iters;
   }
 };
 
@@ -368,11 +396,10 @@ __device__ __forceinline__ void fwd_row(const FwdBuf<C>& b, int64_t r, int slot,
   if (tid == 0) gate[r] = s.g;
 }
 
-template <int W, int C, bool FULL, int D>
+template <int W, int C, bool FULL, int D, bool FUSED>
 __global__ __launch_bounds__(W * kWave) void gate_fwd_kernel(
     const u32x4* __restrict__ x, const u32x4* __restrict__ k,
-    const u32x4* __restrict__ v, const f32x4* __restrict__ wh,
-    const f32x4* __restrict__ we, u32x4* __restrict__ out,
+    const u32x4* __restrict__ v, WeightsIn wts, u32x4* __restrict__ out,
     float* __restrict__ gate, RowWalk walk, int nchunk, double eps, double inv_h,
     double inv_sqrt_h) {
   constexpr int NT = W * kWave;
@@ -380,7 +407,7 @@ __global__ __launch_bounds__(W * kWave) void gate_fwd_kernel(
   __shared__ double red[2][3][W];
 
   const int64_t blk = xcd_slab_block();
-  const int64_t first = blk * walk.block_stride;
+  const int64_t first = walk.first_row(blk);
   const int64_t n = walk.rows_of(first);
   if (n <= 0) return;
   const int64_t step = walk.row_step;
@@ -390,7 +417,7 @@ __global__ __launch_bounds__(W * kWave) void gate_fwd_kernel(
 #pragma unroll
   for (int s = 0; s + 1 < D; ++s) fwd_load<NT, C, FULL>(buf[s], x, k, v, row(s), nchunk, tid);
   WeightsReg<C> w64;
-  load_weights<NT, C, FULL>(wh, we, tid, nchunk, w64.w);
+  load_weights<NT, C, FULL, FUSED>(wts, tid, nchunk, w64.w);
 
   for (int64_t i = 0;; i += D) {
 #pragma unroll
@@ -515,27 +542,40 @@ __device__ __forceinline__ void bwd_row(const BwdBuf<C>& b, int64_t r, int slot,
   }
 }
 
-template <int W, int C, bool FULL, int D, bool WLDS>
+template <int W, int C, bool FULL, int D, bool WLDS, bool FUSED>
 __global__ __launch_bounds__(W * kWave) void gate_bwd_kernel(
     const u32x4* __restrict__ gout, const u32x4* __restrict__ x,
-    const u32x4* __restrict__ k, const u32x4* __restrict__ v,
-    const f32x4* __restrict__ wh, const f32x4* __restrict__ we,
+    const u32x4* __restrict__ k, const u32x4* __restrict__ v, WeightsIn wts,
     u32x4* __restrict__ dx, u32x4* __restrict__ dk, u32x4* __restrict__ dv,
     f32x4* __restrict__ partial, RowWalk walk, int nchunk, double eps,
-    float clamp, double inv_h, double inv_sqrt_h) {
+    float clamp, double inv_h, double inv_sqrt_h, int carry) {
   constexpr int NT = W * kWave;
   const int tid = threadIdx.x;
   __shared__ double red[2][4][W];
 
-  // c_i over this block's rows, for the thread's columns.
+  const int64_t blk = xcd_slab_block();
+  f32x4* prow = partial + blk * (2 * nchunk);
+
+  // c_i over this block's rows, for the thread's columns: from zero in the
+  // first epoch, else from the previous epoch's partial row, so the sum runs
+  // in the same order, with the same fp32 state, as one long walk.
   float cacc[C][8];
 #pragma unroll
-  for (int j = 0; j < C; ++j)
+  for (int j = 0; j < C; ++j) {
+    const int c = j * NT + tid;
+    f32x4 lo = {0.f, 0.f, 0.f, 0.f}, hi = lo;
+    if (carry && (FULL || c < nchunk)) {
+      lo = prow[2 * c];
+      hi = prow[2 * c + 1];
+    }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) cacc[j][e] = 0.f;
+    for (int e = 0; e < 4; ++e) {
+      cacc[j][e] = lo[e];
+      cacc[j][e + 4] = hi[e];
+    }
+  }
 
-  const int64_t blk = xcd_slab_block();
-  const int64_t first = blk * walk.block_stride;
+  const int64_t first = walk.first_row(blk);
   const int64_t n = walk.rows_of(first);
 
   if (n > 0) {
@@ -546,7 +586,7 @@ __global__ __launch_bounds__(W * kWave) void gate_bwd_kernel(
     for (int s = 0; s + 1 < D; ++s)
       bwd_load<NT, C, FULL>(buf[s], gout, x, k, v, row(s), nchunk, tid);
     double w64[C][8];
-    load_weights<NT, C, FULL>(wh, we, tid, nchunk, w64);
+    load_weights<NT, C, FULL, FUSED>(wts, tid, nchunk, w64);
     auto walk_rows = [&](const auto& wts) {
       for (int64_t i = 0;; i += D) {
 #pragma unroll
@@ -574,7 +614,6 @@ __global__ __launch_bounds__(W * kWave) void gate_bwd_kernel(
   }
 
   // This block's partial row of c.
-  f32x4* prow = partial + blk * (2 * nchunk);
 #pragma unroll
   for (int j = 0; j < C; ++j) {
     const int c = j * NT + tid;
@@ -770,13 +809,17 @@ Plan bwd_plan(int nchunk) {
 
 int64_t grid_of(const Plan& p, int64_t T) { return T < p.blocks ? T : p.blocks; }
 
-RowWalk row_walk(int64_t T, int64_t G) {
-  RowWalk w;
-  w.T = T;
-  w.block_stride = 1;
-  w.row_step = G > 0 ? G : 1;
-  w.per_block = G > 0 ? (T + G - 1) / G : 0;
-  return w;
+// Epochs: each launch of a walk covers at most about kEpochBytes of every
+// [T, H] tensor, i.e. at most that many bytes / (G * 2H) rows per block. On
+// MI355X a single launch of many rows per block loses bandwidth as the
+// blocks drift apart (the backward at H = 7168: 0.73 of 8 TB/s at 16384
+// rows, 0.70 at 65536 and 0.64 at 131072 in one launch; the same rows in
+// launches of 16384 keep 0.72-0.73 throughout).
+constexpr int64_t kEpochBytes = (int64_t)240 << 20;
+
+int64_t epoch_iters(int64_t G, int64_t H) {
+  const int64_t e = kEpochBytes / (G * H * 2);
+  return e > 0 ? e : 1;
 }
 
 template <class K>
@@ -788,7 +831,7 @@ tk_status launch(K kernel, int grid, int block, void** args, hipStream_t st) {
 
 struct FwdArgs {
   const u32x4 *x, *k, *v;
-  const f32x4 *wh, *we;
+  WeightsIn wts;
   u32x4* out;
   float* gate;
   RowWalk walk;
@@ -796,82 +839,141 @@ struct FwdArgs {
   double eps, inv_h, inv_sqrt_h;
 };
 
-template <int W, int C, bool FULL, int D>
+template <int W, int C, bool FULL, int D, bool FUSED>
 tk_status run_fwd(FwdArgs a, int grid, hipStream_t st) {
-  void* args[] = {&a.x,    &a.k,      &a.v,   &a.wh,    &a.we,        &a.out,
+  void* args[] = {&a.x,    &a.k,    &a.v,      &a.wts, &a.out,
                   &a.gate, &a.walk, &a.nchunk, &a.eps, &a.inv_h, &a.inv_sqrt_h};
-  return launch(gate_fwd_kernel<W, C, FULL, D>, grid, W * kWave, args, st);
+  return launch(gate_fwd_kernel<W, C, FULL, D, FUSED>, grid, W * kWave, args, st);
 }
 
+template <bool F>
 tk_status dispatch_fwd(const Plan& p, const FwdArgs& a, int grid, hipStream_t st) {
-  if (p.W == 7 && p.C == 2 && p.full && p.D == 2) return run_fwd<7, 2, true, 2>(a, grid, st);
-  if (p.W == 2 && p.C == 4 && p.full && p.D == 3) return run_fwd<2, 4, true, 3>(a, grid, st);
-  if (p.W == 2 && p.C == 5 && p.full && p.D == 3) return run_fwd<2, 5, true, 3>(a, grid, st);
-  if (p.W == 3 && p.C == 2 && p.full && p.D == 3) return run_fwd<3, 2, true, 3>(a, grid, st);
-  if (p.W == 1 && p.C == 4 && p.full && p.D == 2) return run_fwd<1, 4, true, 2>(a, grid, st);
-  if (p.W == 2 && p.C == 6 && p.full && p.D == 2) return run_fwd<2, 6, true, 2>(a, grid, st);
+  if (p.W == 7 && p.C == 2 && p.full && p.D == 2) return run_fwd<7, 2, true, 2, F>(a, grid, st);
+  if (p.W == 2 && p.C == 4 && p.full && p.D == 3) return run_fwd<2, 4, true, 3, F>(a, grid, st);
+  if (p.W == 2 && p.C == 5 && p.full && p.D == 3) return run_fwd<2, 5, true, 3, F>(a, grid, st);
+  if (p.W == 3 && p.C == 2 && p.full && p.D == 3) return run_fwd<3, 2, true, 3, F>(a, grid, st);
+  if (p.W == 1 && p.C == 4 && p.full && p.D == 2) return run_fwd<1, 4, true, 2, F>(a, grid, st);
+  if (p.W == 2 && p.C == 6 && p.full && p.D == 2) return run_fwd<2, 6, true, 2, F>(a, grid, st);
   if (p.D == 2 && p.C == 1) {
     switch (p.W) {
-      case 1: return run_fwd<1, 1, false, 2>(a, grid, st);
-      case 2: return run_fwd<2, 1, false, 2>(a, grid, st);
-      case 4: return run_fwd<4, 1, false, 2>(a, grid, st);
-      case 8: return run_fwd<8, 1, false, 2>(a, grid, st);
+      case 1: return run_fwd<1, 1, false, 2, F>(a, grid, st);
+      case 2: return run_fwd<2, 1, false, 2, F>(a, grid, st);
+      case 4: return run_fwd<4, 1, false, 2, F>(a, grid, st);
+      case 8: return run_fwd<8, 1, false, 2, F>(a, grid, st);
       default: break;
     }
   }
-  if (p.W == 8 && p.C == 2 && p.D == 2) return run_fwd<8, 2, false, 2>(a, grid, st);
+  if (p.W == 8 && p.C == 2 && p.D == 2) return run_fwd<8, 2, false, 2, F>(a, grid, st);
   return TK_ERR_UNSUPPORTED;
 }
 
 struct BwdArgs {
   const u32x4 *g, *x, *k, *v;
-  const f32x4 *wh, *we;
+  WeightsIn wts;
   u32x4 *dx, *dk, *dv;
   f32x4* partial;
   RowWalk walk;
   int nchunk;
   double eps, inv_h, inv_sqrt_h;
   float clamp;
+  int carry;
 };
 
-template <int W, int C, bool FULL, int D, bool WLDS>
+template <int W, int C, bool FULL, int D, bool WLDS, bool FUSED>
 tk_status run_bwd(BwdArgs a, int grid, hipStream_t st) {
-  void* args[] = {&a.g,       &a.x,    &a.k,      &a.v,   &a.wh,
-                  &a.we,      &a.dx,   &a.dk,     &a.dv,  &a.partial,
-                  &a.walk,    &a.nchunk, &a.eps,  &a.clamp, &a.inv_h,
-                  &a.inv_sqrt_h};
-  return launch(gate_bwd_kernel<W, C, FULL, D, WLDS>, grid, W * kWave, args, st);
+  void* args[] = {&a.g,       &a.x,      &a.k,   &a.v,     &a.wts,
+                  &a.dx,      &a.dk,     &a.dv,  &a.partial, &a.walk,
+                  &a.nchunk,  &a.eps,    &a.clamp, &a.inv_h, &a.inv_sqrt_h,
+                  &a.carry};
+  return launch(gate_bwd_kernel<W, C, FULL, D, WLDS, FUSED>, grid, W * kWave, args, st);
 }
 
+template <bool F>
 tk_status dispatch_bwd(const Plan& p, const BwdArgs& a, int grid, hipStream_t st) {
   if (p.W == 7 && p.C == 2 && p.full && p.D == 3 && p.wlds)
-    return run_bwd<7, 2, true, 3, true>(a, grid, st);
+    return run_bwd<7, 2, true, 3, true, F>(a, grid, st);
   if (p.W == 2 && p.C == 4 && p.full && p.D == 2 && !p.wlds)
-    return run_bwd<2, 4, true, 2, false>(a, grid, st);
+    return run_bwd<2, 4, true, 2, false, F>(a, grid, st);
   if (p.W == 2 && p.C == 5 && p.full && p.D == 2 && p.wlds)
-    return run_bwd<2, 5, true, 2, true>(a, grid, st);
+    return run_bwd<2, 5, true, 2, true, F>(a, grid, st);
   if (p.W == 3 && p.C == 2 && p.full && p.D == 2 && !p.wlds)
-    return run_bwd<3, 2, true, 2, false>(a, grid, st);
+    return run_bwd<3, 2, true, 2, false, F>(a, grid, st);
   if (p.W == 1 && p.C == 4 && p.full && p.D == 2 && !p.wlds)
-    return run_bwd<1, 4, true, 2, false>(a, grid, st);
+    return run_bwd<1, 4, true, 2, false, F>(a, grid, st);
   if (p.W == 2 && p.C == 6 && p.full && p.D == 2 && p.wlds)
-    return run_bwd<2, 6, true, 2, true>(a, grid, st);
+    return run_bwd<2, 6, true, 2, true, F>(a, grid, st);
   if (p.D == 2 && !p.wlds && p.C == 1) {
     switch (p.W) {
-      case 1: return run_bwd<1, 1, false, 2, false>(a, grid, st);
-      case 2: return run_bwd<2, 1, false, 2, false>(a, grid, st);
-      case 4: return run_bwd<4, 1, false, 2, false>(a, grid, st);
-      case 8: return run_bwd<8, 1, false, 2, false>(a, grid, st);
+      case 1: return run_bwd<1, 1, false, 2, false, F>(a, grid, st);
+      case 2: return run_bwd<2, 1, false, 2, false, F>(a, grid, st);
+      case 4: return run_bwd<4, 1, false, 2, false, F>(a, grid, st);
+      case 8: return run_bwd<8, 1, false, 2, false, F>(a, grid, st);
       default: break;
     }
   }
   if (p.W == 8 && p.C == 2 && p.D == 2 && !p.wlds)
-    return run_bwd<8, 2, false, 2, false>(a, grid, st);
+    return run_bwd<8, 2, false, 2, false, F>(a, grid, st);
   return TK_ERR_UNSUPPORTED;
 }
 
+// The weights as the kernels take them: wh and we, or the fused weight w.
+WeightsIn weights_in(const float* wh, const float* we, const double* w) {
+  return {reinterpret_cast<const f32x4*>(wh), reinterpret_cast<const f32x4*>(we),
+          reinterpret_cast<const f64x2*>(w)};
+}
+
+// Argument checks of the forward; w1 and w2 are wh and we, or the fused
+// weight twice.
+tk_status check_fwd_args(const uint16_t* x, const uint16_t* k, const uint16_t* v,
+                         const void* w1, const void* w2, const uint16_t* out,
+                         const float* gate, int64_t T, int64_t H, double eps) {
+  tk_status st = check_shape(T, H);
+  if (st != TK_SUCCESS) return st;
+  if (!finite_positive(eps)) return TK_ERR_VALUE;
+  if (T == 0) return TK_SUCCESS;
+  if (!x || !k || !v || !w1 || !w2 || !out || !gate) return TK_ERR_NULL;
+  if (!aligned16(x) || !aligned16(k) || !aligned16(v) || !aligned16(w1) ||
+      !aligned16(w2) || !aligned16(out) || ((uintptr_t)gate & 3u))
+    return TK_ERR_ALIGN;
+  return TK_SUCCESS;
+}
+
+// The forward's launches once its arguments are checked; T > 0.
+tk_status enqueue_fwd(const uint16_t* x, const uint16_t* k, const uint16_t* v,
+                      WeightsIn wts, uint16_t* out, float* gate, int64_t T, int64_t H,
+                      double eps, hipStream_t st) {
+  const int nchunk = (int)(H / 8);
+  FwdArgs a;
+  a.x = reinterpret_cast<const u32x4*>(x);
+  a.k = reinterpret_cast<const u32x4*>(k);
+  a.v = reinterpret_cast<const u32x4*>(v);
+  a.wts = wts;
+  a.out = reinterpret_cast<u32x4*>(out);
+  a.gate = gate;
+  const Plan plan = fwd_plan(nchunk);
+  const int grid = (int)grid_of(plan, T);
+  a.nchunk = nchunk;
+  a.eps = eps;
+  a.inv_h = 1.0 / (double)H;
+  a.inv_sqrt_h = 1.0 / std::sqrt((double)H);
+  const int64_t per_block = (T + grid - 1) / grid;
+  const int64_t E = epoch_iters(grid, H);
+  a.walk.T = T;
+  a.walk.row_step = grid;
+  for (int64_t i0 = 0; i0 < per_block; i0 += E) {
+    a.walk.iter0 = i0;
+    a.walk.iters = std::min(E, per_block - i0);
+    const tk_status s =
+        wts.w ? dispatch_fwd<true>(plan, a, grid, st) : dispatch_fwd<false>(plan, a, grid, st);
+    if (s != TK_SUCCESS) return s;
+  }
+  return TK_SUCCESS;
+}
+
+// Argument checks of the backward (but its workspace); wh and we, or the
+// fused weight twice.
 tk_status check_bwd_args(const uint16_t* grad_out, const uint16_t* x, const uint16_t* k,
-                         const uint16_t* v, const float* wh, const float* we,
+                         const uint16_t* v, const void* wh, const void* we,
                          const uint16_t* dx, const uint16_t* dk, const uint16_t* dv,
                          int64_t T, int64_t H, double eps, double dsqrt_clamp) {
   tk_status st = check_shape(T, H);
@@ -887,7 +989,7 @@ tk_status check_bwd_args(const uint16_t* grad_out, const uint16_t* x, const uint
 
 // The backward's launch once its arguments are checked; T > 0.
 tk_status enqueue_bwd(const uint16_t* grad_out, const uint16_t* x, const uint16_t* k,
-                      const uint16_t* v, const float* wh, const float* we, uint16_t* dx,
+                      const uint16_t* v, WeightsIn wts, uint16_t* dx,
                       uint16_t* dk, uint16_t* dv, float* partial, int64_t T, int64_t H,
                       double eps, double dsqrt_clamp, hipStream_t st) {
   const int nchunk = (int)(H / 8);
@@ -896,21 +998,33 @@ tk_status enqueue_bwd(const uint16_t* grad_out, const uint16_t* x, const uint16_
   a.x = reinterpret_cast<const u32x4*>(x);
   a.k = reinterpret_cast<const u32x4*>(k);
   a.v = reinterpret_cast<const u32x4*>(v);
-  a.wh = reinterpret_cast<const f32x4*>(wh);
-  a.we = reinterpret_cast<const f32x4*>(we);
+  a.wts = wts;
   a.dx = reinterpret_cast<u32x4*>(dx);
   a.dk = reinterpret_cast<u32x4*>(dk);
   a.dv = reinterpret_cast<u32x4*>(dv);
   a.partial = reinterpret_cast<f32x4*>(partial);
   const Plan plan = bwd_plan(nchunk);
   const int grid = (int)grid_of(plan, T);
-  a.walk = row_walk(T, grid);
   a.nchunk = nchunk;
   a.eps = eps;
   a.clamp = (float)dsqrt_clamp;
   a.inv_h = 1.0 / (double)H;
   a.inv_sqrt_h = 1.0 / std::sqrt((double)H);
-  return dispatch_bwd(plan, a, grid, st);
+  // the walk in epochs; every epoch after the first continues the partial
+  // sums the previous one left in `partial`
+  const int64_t per_block = (T + grid - 1) / grid;
+  const int64_t E = epoch_iters(grid, H);
+  a.walk.T = T;
+  a.walk.row_step = grid;
+  for (int64_t i0 = 0; i0 < per_block; i0 += E) {
+    a.walk.iter0 = i0;
+    a.walk.iters = std::min(E, per_block - i0);
+    a.carry = i0 > 0;
+    const tk_status s =
+        wts.w ? dispatch_bwd<true>(plan, a, grid, st) : dispatch_bwd<false>(plan, a, grid, st);
+    if (s != TK_SUCCESS) return s;
+  }
+  return TK_SUCCESS;
 }
 
 // The reduction's launch once its arguments are checked.
@@ -971,6 +1085,15 @@ int64_t tk_engram_num_partials(int64_t T, int64_t H) {
   return grid_of(bwd_plan((int)(H / 8)), T);
 }
 
+int64_t tk_engram_gate_launches(int64_t T, int64_t H, int32_t backward) {
+  if (check_shape(T, H) != TK_SUCCESS || T == 0) return 0;
+  const int nchunk = (int)(H / 8);
+  const int64_t grid = grid_of(backward ? bwd_plan(nchunk) : fwd_plan(nchunk), T);
+  const int64_t per_block = (T + grid - 1) / grid;
+  const int64_t E = epoch_iters(grid, H);
+  return (per_block + E - 1) / E;
+}
+
 size_t tk_engram_bwd_workspace_bytes(int64_t T, int64_t H) {
   if (check_shape(T, H) != TK_SUCCESS) return 0;
   return (size_t)tk_engram_num_partials(T, H) * (size_t)H * sizeof(float);
@@ -980,31 +1103,20 @@ tk_status tk_engram_gate_fwd(const uint16_t* x, const uint16_t* k,
                              const uint16_t* v, const float* wh,
                              const float* we, uint16_t* out, float* gate,
                              int64_t T, int64_t H, double eps, void* stream) {
-  tk_status st = check_shape(T, H);
-  if (st != TK_SUCCESS) return st;
-  if (!finite_positive(eps)) return TK_ERR_VALUE;
-  if (T == 0) return TK_SUCCESS;
-  if (!x || !k || !v || !wh || !we || !out || !gate) return TK_ERR_NULL;
-  if (!aligned16(x) || !aligned16(k) || !aligned16(v) || !aligned16(wh) ||
-      !aligned16(we) || !aligned16(out) || ((uintptr_t)gate & 3u))
-    return TK_ERR_ALIGN;
-  const int nchunk = (int)(H / 8);
-  FwdArgs a;
-  a.x = reinterpret_cast<const u32x4*>(x);
-  a.k = reinterpret_cast<const u32x4*>(k);
-  a.v = reinterpret_cast<const u32x4*>(v);
-  a.wh = reinterpret_cast<const f32x4*>(wh);
-  a.we = reinterpret_cast<const f32x4*>(we);
-  a.out = reinterpret_cast<u32x4*>(out);
-  a.gate = gate;
-  const Plan plan = fwd_plan(nchunk);
-  const int grid = (int)grid_of(plan, T);
-  a.walk = row_walk(T, grid);
-  a.nchunk = nchunk;
-  a.eps = eps;
-  a.inv_h = 1.0 / (double)H;
-  a.inv_sqrt_h = 1.0 / std::sqrt((double)H);
-  return dispatch_fwd(plan, a, grid, reinterpret_cast<hipStream_t>(stream));
+  const tk_status st = check_fwd_args(x, k, v, wh, we, out, gate, T, H, eps);
+  if (st != TK_SUCCESS || T == 0) return st;
+  return enqueue_fwd(x, k, v, weights_in(wh, we, nullptr), out, gate, T, H, eps,
+                     reinterpret_cast<hipStream_t>(stream));
+}
+
+tk_status tk_engram_gate_fwd_fused(const uint16_t* x, const uint16_t* k,
+                                   const uint16_t* v, const double* w, uint16_t* out,
+                                   float* gate, int64_t T, int64_t H, double eps,
+                                   void* stream) {
+  const tk_status st = check_fwd_args(x, k, v, w, w, out, gate, T, H, eps);
+  if (st != TK_SUCCESS || T == 0) return st;
+  return enqueue_fwd(x, k, v, weights_in(nullptr, nullptr, w), out, gate, T, H, eps,
+                     reinterpret_cast<hipStream_t>(stream));
 }
 
 tk_status tk_engram_gate_bwd(const uint16_t* grad_out, const uint16_t* x,
@@ -1018,8 +1130,22 @@ tk_status tk_engram_gate_bwd(const uint16_t* grad_out, const uint16_t* x,
   if (!workspace) return TK_ERR_NULL;
   if (!aligned16(workspace)) return TK_ERR_ALIGN;
   if (workspace_bytes < tk_engram_bwd_workspace_bytes(T, H)) return TK_ERR_WORKSPACE;
-  return enqueue_bwd(grad_out, x, k, v, wh, we, dx, dk, dv, workspace, T, H, eps,
-                     dsqrt_clamp, reinterpret_cast<hipStream_t>(stream));
+  return enqueue_bwd(grad_out, x, k, v, weights_in(wh, we, nullptr), dx, dk, dv, workspace,
+                     T, H, eps, dsqrt_clamp, reinterpret_cast<hipStream_t>(stream));
+}
+
+tk_status tk_engram_gate_bwd_fused(const uint16_t* grad_out, const uint16_t* x,
+                                   const uint16_t* k, const uint16_t* v, const double* w,
+                                   uint16_t* dx, uint16_t* dk, uint16_t* dv, float* workspace,
+                                   size_t workspace_bytes, int64_t T, int64_t H, double eps,
+                                   double dsqrt_clamp, void* stream) {
+  tk_status st = check_bwd_args(grad_out, x, k, v, w, w, dx, dk, dv, T, H, eps, dsqrt_clamp);
+  if (st != TK_SUCCESS || T == 0) return st;
+  if (!workspace) return TK_ERR_NULL;
+  if (!aligned16(workspace)) return TK_ERR_ALIGN;
+  if (workspace_bytes < tk_engram_bwd_workspace_bytes(T, H)) return TK_ERR_WORKSPACE;
+  return enqueue_bwd(grad_out, x, k, v, weights_in(nullptr, nullptr, w), dx, dk, dv,
+                     workspace, T, H, eps, dsqrt_clamp, reinterpret_cast<hipStream_t>(stream));
 }
 
 tk_status tk_engram_grad_w_reduce(const float* workspace, int64_t P, int64_t H,
@@ -1053,7 +1179,8 @@ tk_status tk_engram_gate_bwd_reduce_noalloc(const uint16_t* grad_out, const uint
   st = scratch_of(hs, &partial);
   if (st != TK_SUCCESS) return st;
   if (T > 0) {
-    st = enqueue_bwd(grad_out, x, k, v, wh, we, dx, dk, dv, partial, T, H, eps, dsqrt_clamp, hs);
+    st = enqueue_bwd(grad_out, x, k, v, weights_in(wh, we, nullptr), dx, dk, dv, partial, T, H,
+                     eps, dsqrt_clamp, hs);
     if (st != TK_SUCCESS) return st;
   }
   return enqueue_reduce(partial, tk_engram_num_partials(T, H), H, wh, we, dwh, dwe, hs);

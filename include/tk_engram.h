@@ -44,8 +44,12 @@
  *     only on (T, H), and no atomics are used, so reruns are bit-identical.
  *   - Errors: arguments are checked before any device work; a failed check
  *     returns its status and enqueues nothing. A launch failure returns
- *     TK_ERR_LAUNCH. Faults inside kernels surface at the caller's next
+ *     TK_ERR_LAUNCH (a call of several launches leaves the ones before it
+ *     enqueued). Faults inside kernels surface at the caller's next
  *     synchronisation, as for any HIP kernel.
+ *   - The gate calls walk long batches in several launches (epochs of about
+ *     240 MB of each [T, H] tensor) on `stream`; the split depends only on
+ *     (T, H) and does not change any result bit.
  *   - Shape limits of the gate calls: 0 <= T, 8 <= H <= 8192, H a multiple
  *     of 8; T = 0 is a successful no-op. The hash and the gather state
  *     their own limits below.
@@ -102,6 +106,14 @@ tk_status tk_engram_gate_fwd(const uint16_t* x, const uint16_t* k,
  * each). A pure function of (T, H), at most T; 0 when T = 0.
  */
 int64_t tk_engram_num_partials(int64_t T, int64_t H);
+
+/*
+ * Number of kernel launches tk_engram_gate_fwd (backward = 0) or
+ * tk_engram_gate_bwd (backward != 0), and their _fused forms, enqueue for
+ * (T, H): the row walk split into epochs of about 240 MB of each [T, H]
+ * tensor. A pure function of (T, H); 0 when T = 0 or the shape is invalid.
+ */
+int64_t tk_engram_gate_launches(int64_t T, int64_t H, int32_t backward);
 
 /* Bytes of backward workspace needed for (T, H): P * H * sizeof(float). */
 size_t tk_engram_bwd_workspace_bytes(int64_t T, int64_t H);
@@ -202,12 +214,35 @@ tk_status tk_engram_gate_bwd_reduce_noalloc(const uint16_t* grad_out, const uint
  *   wh, we : fp32 [H], device, 4-byte aligned
  *   w      : fp64 [H], device, 8-byte aligned
  *
- * The gate calls above form the same exact products themselves (they are
- * O(H) per launch), so they take wh and we; this call is for callers that
- * keep the fused weight. H = 0 is a successful no-op.
+ * tk_engram_gate_fwd_fused and tk_engram_gate_bwd_fused below take w in
+ * place of wh and we; tk_engram_gate_fwd and tk_engram_gate_bwd form the same
+ * exact products themselves (O(H) per launch). H = 0 is a successful no-op.
  */
 tk_status tk_engram_fused_weight(const float* wh, const float* we, double* w, int64_t H,
                                  void* stream);
+
+/*
+ * The forward and the backward with the fused RMSNorm weight (section
+ * "5. Engram": engram_fused_weight, then the gate): w = wh * we, fp64 [H],
+ * device, 16-byte aligned, in place of wh and we; every other argument,
+ * limit and error as for tk_engram_gate_fwd and tk_engram_gate_bwd. With w
+ * from tk_engram_fused_weight(wh, we) the results are those of the unfused
+ * calls bit for bit: the unfused kernels form exactly this w. The
+ * weight-gradient reduction still needs wh and we separately (dL/dwh = we *
+ * c, dL/dwe = wh * c), so it takes them as before. For any other fp64 w the
+ * calls compute the gate with that weight product; the elementwise backward
+ * rounds it to fp32.
+ */
+tk_status tk_engram_gate_fwd_fused(const uint16_t* x, const uint16_t* k,
+                                   const uint16_t* v, const double* w, uint16_t* out,
+                                   float* gate, int64_t T, int64_t H, double eps,
+                                   void* stream);
+
+tk_status tk_engram_gate_bwd_fused(const uint16_t* grad_out, const uint16_t* x,
+                                   const uint16_t* k, const uint16_t* v, const double* w,
+                                   uint16_t* dx, uint16_t* dk, uint16_t* dv, float* workspace,
+                                   size_t workspace_bytes, int64_t T, int64_t H, double eps,
+                                   double dsqrt_clamp, void* stream);
 
 /*
  * N-gram hash of the Engram memory (section "5. Engram": engram_hash, the

@@ -60,6 +60,22 @@ def test_partials_are_a_function_of_shape():
     assert eg.tk_engram_num_partials(-1, 64) == 0
 
 
+def test_launch_counts_are_a_function_of_shape():
+    # the row walk in epochs of about 240 MB of each [T, H] tensor
+    assert eg.tk_engram_gate_launches(0, 7168, True) == 0
+    assert eg.tk_engram_gate_launches(64, 12, False) == 0
+    for backward in (False, True):
+        assert eg.tk_engram_gate_launches(1024, 4096, backward) == 1
+        assert eg.tk_engram_gate_launches(16384, 4096, backward) == 1
+        # H = 7168: 224 blocks, 240 MiB / (224 * 14336 B) = 78 rows per block
+        assert eg.tk_engram_gate_launches(224 * 78, 7168, backward) == 1
+        assert eg.tk_engram_gate_launches(224 * 78 + 1, 7168, backward) == 2
+        assert eg.tk_engram_gate_launches(32768, 7168, backward) == 2
+        assert eg.tk_engram_gate_launches(65537, 7168, backward) == 4
+        # H = 4096: 256 blocks, 120 rows per block
+        assert eg.tk_engram_gate_launches(40000, 4096, backward) == 2
+
+
 def fwd(**kw):
     a = dict(x=A16, k=A16, v=A16, wh=A16, we=A16, out=A16, gate=A16, T=4, H=64,
              eps=1e-6)

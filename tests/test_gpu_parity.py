@@ -59,28 +59,37 @@ def same_bits(a, b):
     return torch.equal(a.view(view), b.view(view))
 
 
-def run_gpu(eg, d, dev, backward=True, rerun=False):
+def run_gpu(eg, d, dev, backward=True, rerun=False, fused=False):
     """Forward (+ backward + reduction) on the GPU; returns host arrays. With
     `rerun`, every call runs a second time into fresh outputs, and each
-    output must equal the first run's bit for bit."""
+    output must equal the first run's bit for bit. With `fused`, the forward
+    and the backward take the fused weight w = wh * we from
+    tk_engram_fused_weight instead of wh and we."""
     import torch
     T, H = d["x"].shape
     x, k, v = to_dev(d["x"], dev), to_dev(d["k"], dev), to_dev(d["v"], dev)
     wh = torch.from_numpy(d["wh"]).to(dev)
     we = torch.from_numpy(d["we"]).to(dev)
-    out, gate = eg.tk_engram_gate_fwd(x, k, v, wh, we)
+    if fused:
+        w = eg.tk_engram_fused_weight(wh, we)
+        fwd = lambda: eg.tk_engram_gate_fwd_fused(x, k, v, w)  # noqa: E731
+        bwd = lambda g: eg.tk_engram_gate_bwd_fused(g, x, k, v, w)  # noqa: E731
+    else:
+        fwd = lambda: eg.tk_engram_gate_fwd(x, k, v, wh, we)  # noqa: E731
+        bwd = lambda g: eg.tk_engram_gate_bwd(g, x, k, v, wh, we)  # noqa: E731
+    out, gate = fwd()
     if rerun:
-        out2, gate2 = eg.tk_engram_gate_fwd(x, k, v, wh, we)
+        out2, gate2 = fwd()
         torch.cuda.synchronize()
         assert same_bits(out, out2) and same_bits(gate, gate2), "forward rerun differs"
         del out2, gate2
     res = {}
     if backward:
         g = to_dev(d["grad_out"], dev)
-        dx, dk, dv, ws, P = eg.tk_engram_gate_bwd(g, x, k, v, wh, we)
+        dx, dk, dv, ws, P = bwd(g)
         dwh, dwe = eg.tk_engram_grad_w_reduce(ws, P, H, wh, we)
         if rerun:
-            again = eg.tk_engram_gate_bwd(g, x, k, v, wh, we)
+            again = bwd(g)
             again_w = eg.tk_engram_grad_w_reduce(again[3], P, H, wh, we)
             torch.cuda.synchronize()
             for name, a, b in (("dx", dx, again[0]), ("dk", dk, again[1]), ("dv", dv, again[2]),
@@ -213,6 +222,22 @@ def test_full_size(eg, cuda_device, cfg):
     say(f"[config {cfg}] GPU done (P={g['P']}), comparing with the oracle")
     assert_report(compare(d, g), name=c.name)
     assert_dv_is_gate_times_grad(d, g)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("cfg", [1, 4])
+def test_fused_weight_calls_match_the_oracle_and_the_unfused_calls(eg, cuda_device, cfg):
+    # engram_fused_weight of the "5. Engram" section feeding the gate: the
+    # forward and the backward that read w = wh * we give the unfused calls'
+    # results bit for bit, and so meet the oracle's tolerances
+    c = synth.CONFIGS[cfg]
+    say(f"[config {cfg}] {c.name}: fused-weight calls, T={c.T} H={c.H}")
+    d = synth.make_inputs(cfg)
+    gf = run_gpu(eg, d, cuda_device, fused=True)
+    gu = run_gpu(eg, d, cuda_device)
+    for name in ("out", "gate", "dx", "dk", "dv", "dwh", "dwe"):
+        assert np.array_equal(gf[name].view(np.uint8), gu[name].view(np.uint8)), name
+    assert_report(compare(d, gf), name=c.name + " (fused weight)")
 
 
 @pytest.mark.timeout(900)
@@ -383,11 +408,15 @@ def test_derivative_clamp_region(eg, cuda_device):
         assert np.all(rel <= REL_TOL), (name, np.flatnonzero(rel > REL_TOL), z)
 
 
-@pytest.mark.parametrize("T,H", [(1000, 4096), (500, 7168), (37, 256)])
+@pytest.mark.parametrize("T,H", [(1000, 4096), (500, 7168), (37, 256), (40000, 4096),
+                                 (20000, 7168)])
 def test_workspace_holds_the_documented_partials(eg, cuda_device, T, H):
     """The header's contract for the backward's workspace: partial row p is
     c_p[i] = sum over t = p, p + P, ... of dd_t r_x,t r_k,t x_t,i k_t,i,
-    rebuilt here in fp64 from the oracle's per-token scalars."""
+    rebuilt here in fp64 from the oracle's per-token scalars. The last two
+    shapes walk their rows in two launches each, the second one short
+    (157 = 120 + 37 rows per block at H = 4096, 90 = 78 + 12 at H = 7168), so
+    the partial sums carry over a launch boundary."""
     import torch
     d = make_case(T, H, seed=T + H)
     dev = cuda_device
@@ -404,8 +433,8 @@ def test_workspace_holds_the_documented_partials(eg, cuda_device, T, H):
                                         d["we"], want_grads=False)
     A = dd * fst[:, 2] * fst[:, 3]                    # dd r_x r_k per token
     want = np.zeros((P, H))
-    for t in range(T):
-        want[t % P] += A[t] * xf[t] * kf[t]
+    for p in range(P):
+        want[p] = (A[p::P, None] * xf[p::P] * kf[p::P]).sum(axis=0)
     rel = np.linalg.norm(got - want) / np.linalg.norm(want)
     say(f"[workspace T={T} H={H} P={P}] rel L2 {rel:.3e}")
     assert rel <= 1e-5

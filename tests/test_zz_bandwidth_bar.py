@@ -19,7 +19,7 @@ BAR = 0.70
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("cfg", [3, 4])
+@pytest.mark.parametrize("cfg", [3, 4, 5])
 def test_forward_and_backward_reach_70_percent_of_hbm(cuda_device, cfg):
     import torch
     sys.path.insert(0, ROOT)
