@@ -899,7 +899,7 @@ def measured_traffic(kernel: str, workload: str):
     if rec.get("kernel_source_sha256_16") != kernel_source_hash():
         return None
     k = rec.get("kernels", {}).get(kernel)
-    return None if k is None else k.get("bytes_per_launch")
+    return None if k is None else k.get("bytes_per_call")
 
 
 def read_counter_csv(path: str, counter: str) -> dict:
@@ -948,7 +948,7 @@ def traffic_from_counters(fetch_csv: str, write_csv: str, workload: int) -> dict
         rd = fetch[k] * 1024.0 * f_scale
         wr = write[k] * 1024.0 * w_scale
         kernels[k] = {"fetch_kib_per_call": fetch[k], "write_kib_per_call": write[k],
-                      "read_bytes": rd, "write_bytes": wr, "bytes_per_launch": rd + wr,
+                      "read_bytes": rd, "write_bytes": wr, "bytes_per_call": rd + wr,
                       "algorithmic_bytes": algo.get(k),
                       "measured_over_algorithmic": (rd + wr) / algo[k] if k in algo else None}
     rec = {"workload": c.name, "T": c.T, "H": c.H, "launches_per_call": per_call,

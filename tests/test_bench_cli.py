@@ -39,26 +39,28 @@ def test_traffic_summary_calibrates_on_the_copy_probe(tmp_path, monkeypatch):
     fwd = "void (anonymous namespace)::gate_fwd_kernel<7, 2, true, 2>(unsigned int, int)"
     bwd = "void (anonymous namespace)::gate_bwd_kernel<7, 2, true, 3, true>(int)"
     cp = "(anonymous namespace)::copy_probe_kernel(unsigned int __vector(4) const*, long)"
-    # FETCH_SIZE reads half the bytes and WRITE_SIZE all of them, in KiB
+    # FETCH_SIZE reads half the bytes and WRITE_SIZE all of them, in KiB; at
+    # this shape each gate call is two epoch launches, each with half its bytes
+    assert bench.gate_launches(c.T, c.H) == {"gate_fwd_kernel": 2, "gate_bwd_kernel": 2}
     _counter_csv(tmp_path / "f.csv", "FETCH_SIZE",
-                 [(cp, copy_bytes / 2048), (fwd, 3 * copy_bytes / 2 / 2048),
-                  (fwd, 3 * copy_bytes / 2 / 2048), (bwd, 2 * copy_bytes / 2048)])
+                 [(cp, copy_bytes / 2048)] + [(fwd, 3 * copy_bytes / 4 / 2048)] * 4
+                 + [(bwd, copy_bytes / 2048)] * 2)
     _counter_csv(tmp_path / "w.csv", "WRITE_SIZE",
-                 [(cp, copy_bytes / 1024), (fwd, copy_bytes / 2 / 1024),
-                  (bwd, 3 * copy_bytes / 2 / 1024)])
+                 [(cp, copy_bytes / 1024)] + [(fwd, copy_bytes / 4 / 1024)] * 2
+                 + [(bwd, 3 * copy_bytes / 4 / 1024)] * 2)
     monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
     rec = bench.traffic_from_counters(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), 4)
     assert abs(rec["calibration"]["fetch_scale"] - 2.0) < 1e-12
     assert abs(rec["calibration"]["write_scale"] - 1.0) < 1e-12
     k = rec["kernels"]
     # forward: 3 tensors read, 1 written; backward: 4 read, 3 written
-    assert abs(k["gate_fwd_kernel"]["bytes_per_launch"] - 2 * copy_bytes) < 1
-    assert abs(k["gate_bwd_kernel"]["bytes_per_launch"] - 3.5 * copy_bytes) < 1
+    assert abs(k["gate_fwd_kernel"]["bytes_per_call"] - 2 * copy_bytes) < 1
+    assert abs(k["gate_bwd_kernel"]["bytes_per_call"] - 3.5 * copy_bytes) < 1
     saved = json.load(open(tmp_path / f"traffic_{c.name}.json"))
     assert saved["kernel_source_sha256_16"] == bench.kernel_source_hash()
     # the bench line uses it only while the kernel source is unchanged
     assert bench.measured_traffic("gate_bwd_kernel", c.name) == \
-        k["gate_bwd_kernel"]["bytes_per_launch"]
+        k["gate_bwd_kernel"]["bytes_per_call"]
     saved["kernel_source_sha256_16"] = "0" * 16
     json.dump(saved, open(tmp_path / f"traffic_{c.name}.json", "w"))
     assert bench.measured_traffic("gate_bwd_kernel", c.name) is None
@@ -151,7 +153,9 @@ def test_footprint_summary_attributes_dispatches(tmp_path, monkeypatch):
         rows = [(cp, copy_bytes / scale / 1024)]
         for T in bench.FOOTPRINT_COUNTER_TOKENS:
             part = (8 if counter == "FETCH_SIZE" else 6) * T * H
-            rows += [(bk, part / scale / 1024)] * n + [(pk, 1.1 * part / scale / 1024)] * n
+            L = bench.gate_launches(T, H)["gate_bwd_kernel"]    # epoch launches per call
+            rows += [(bk, part / L / scale / 1024)] * (n * L)
+            rows += [(pk, 1.1 * part / scale / 1024)] * n
         with open(tmp_path / f"{counter}.csv", "w", newline="") as f:
             w = csv.DictWriter(f, fieldnames=fields)
             w.writeheader()
