@@ -187,8 +187,9 @@ tk_status tk_engram_grad_w_reduce(const float* workspace, int64_t P, int64_t H,
  * TK_ENGRAM_NOALLOC_SCRATCH_BYTES (8 MiB), enough for every (T, H) the gate
  * calls accept; a shape needing more returns TK_ERR_WORKSPACE. Each GPU the
  * library runs on holds its own copy until the process ends; its address is
- * looked up once per device, on the first call there. The call allocates
- * nothing and writes no memset. Every call on one GPU shares that GPU's
+ * looked up once per device (hipGetSymbolAddress), on the first call there,
+ * so make that first call (T = 0 will do) before capturing a HIP graph. The
+ * call allocates nothing and writes no memset. Every call on one GPU shares that GPU's
  * array, which keeps the last call's partials: the backward writes every
  * partial it uses, so nothing needs clearing, but calls that overlap on one
  * GPU (two streams in flight at once) race and must be serialised by the

@@ -46,8 +46,9 @@ def same_bits(a, b):
 
 
 @pytest.mark.parametrize("T,H", [(1001, 7168), (37, 520), (4099, 4096), (3, 8), (257, 2048),
-                                 (129, 6144)])
+                                 (129, 6144), (20003, 7168), (35001, 4096)])
 def test_gate_calls_write_only_their_outputs(eg, cuda_device, T, H):
+    # the last two shapes walk their rows in two launches, the second short
     import torch
     dev = cuda_device
     r = np.random.default_rng(T * 31 + H)
@@ -85,6 +86,57 @@ def test_gate_calls_write_only_their_outputs(eg, cuda_device, T, H):
     assert P2 == P
     for name, want in (("out", out), ("gate", gate), ("dx", dx), ("dk", dk), ("dv", dv),
                        ("dwh", dwh), ("dwe", dwe)):
+        assert same_bits(view[name], want.reshape(-1)), name
+    assert same_bits(view["ws"], ws[:P].reshape(-1))
+
+
+@pytest.mark.parametrize("T,H", [(20003, 7168), (37, 520), (1001, 7168)])
+def test_fused_and_noalloc_calls_write_only_their_outputs(eg, cuda_device, T, H):
+    # the fused-weight forward and backward, and the backward + reduction
+    # with library-owned partials, into windows of marked buffers; each must
+    # equal the plain calls bit for bit
+    import torch
+    dev = cuda_device
+    r = np.random.default_rng(T * 7 + H)
+
+    def up(a):
+        return torch.from_numpy(synth.round_bf16(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    x, k, v, g = (up(r.standard_normal((T, H))) for _ in range(4))
+    wh = torch.from_numpy((1 + 0.1 * r.standard_normal(H)).astype(np.float32)).to(dev)
+    we = torch.from_numpy((1 + 0.1 * r.standard_normal(H)).astype(np.float32)).to(dev)
+    w = eg.tk_engram_fused_weight(wh, we)
+    P = eg.tk_engram_num_partials(T, H)
+    fill_b, fill_f = 0x7FC1, 0x7FC00001
+    bufs = {}
+    for name, n, dt, fill in (("out", T * H, torch.bfloat16, fill_b),
+                              ("gate", T, torch.float32, fill_f),
+                              ("dx", T * H, torch.bfloat16, fill_b),
+                              ("dk", T * H, torch.bfloat16, fill_b),
+                              ("dv", T * H, torch.bfloat16, fill_b),
+                              ("ws", P * H, torch.float32, fill_f),
+                              ("ndx", T * H, torch.bfloat16, fill_b),
+                              ("ndk", T * H, torch.bfloat16, fill_b),
+                              ("ndv", T * H, torch.bfloat16, fill_b),
+                              ("ndwh", H, torch.float32, fill_f),
+                              ("ndwe", H, torch.float32, fill_f)):
+        bufs[name] = (*padded(n, dt, dev, fill), fill)
+    view = {n: b[1] for n, b in bufs.items()}
+    eg.tk_engram_gate_fwd_fused(x, k, v, w, out=view["out"].view(T, H), gate=view["gate"])
+    eg.tk_engram_gate_bwd_fused(g, x, k, v, w, dx=view["dx"].view(T, H),
+                                dk=view["dk"].view(T, H), dv=view["dv"].view(T, H),
+                                workspace=view["ws"].view(P, H))
+    eg.tk_engram_gate_bwd_reduce_noalloc(g, x, k, v, wh, we, dx=view["ndx"].view(T, H),
+                                         dk=view["ndk"].view(T, H), dv=view["ndv"].view(T, H),
+                                         dwh=view["ndwh"], dwe=view["ndwe"])
+    torch.cuda.synchronize()
+    for name, (buf, _, fill) in bufs.items():
+        assert margins_intact(buf, fill), f"{name}: a write landed outside the output"
+    out, gate = eg.tk_engram_gate_fwd(x, k, v, wh, we)
+    dx, dk, dv, ws, _ = eg.tk_engram_gate_bwd(g, x, k, v, wh, we)
+    dwh, dwe = eg.tk_engram_grad_w_reduce(ws, P, H, wh, we)
+    torch.cuda.synchronize()
+    for name, want in (("out", out), ("gate", gate), ("dx", dx), ("dk", dk), ("dv", dv),
+                       ("ndx", dx), ("ndk", dk), ("ndv", dv), ("ndwh", dwh), ("ndwe", dwe)):
         assert same_bits(view[name], want.reshape(-1)), name
     assert same_bits(view["ws"], ws[:P].reshape(-1))
 

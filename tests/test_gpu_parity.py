@@ -591,11 +591,17 @@ def test_fused_weight_is_the_exact_product(eg, cuda_device, H):
 
 # ----------------------------------------------------------------- HIP graphs
 
-def test_graph_capture_and_replay(eg, cuda_device):
-    """The three gate calls allocate nothing and write no memset, so a step
-    captured into a HIP graph replays bit for bit like the eager calls."""
+@pytest.mark.parametrize("T,H,form", [(1000, 7168, "plain"), (20003, 7168, "plain"),
+                                      (20003, 7168, "fused+noalloc"), (1000, 4096,
+                                                                        "fused+noalloc")])
+def test_graph_capture_and_replay(eg, cuda_device, T, H, form):
+    """The gate calls allocate nothing and write no memset, so a step
+    captured into a HIP graph replays bit for bit like the eager calls: the
+    three plain calls, or the fused-weight forward and the backward +
+    reduction with library-owned partials (for callers that cannot allocate,
+    such as code under graph capture). At 20003 x 7168 each gate call is two
+    launches (epochs)."""
     import torch
-    T, H = 1000, 7168
     d = make_case(T, H, seed=21)
     dev = cuda_device
     x, k, v, gout = (to_dev(d[n], dev) for n in ("x", "k", "v", "grad_out"))
@@ -609,10 +615,16 @@ def test_graph_capture_and_replay(eg, cuda_device):
     dwh = torch.empty((H,), dtype=torch.float32, device=dev)
     dwe = torch.empty((H,), dtype=torch.float32, device=dev)
 
+    w = eg.tk_engram_fused_weight(wh, we)
+
     def step():
-        eg.tk_engram_gate_fwd(x, k, v, wh, we, out, gate)
-        eg.tk_engram_gate_bwd(gout, x, k, v, wh, we, dx, dk, dv, ws)
-        eg.tk_engram_grad_w_reduce(ws, P, H, wh, we, dwh, dwe)
+        if form == "plain":
+            eg.tk_engram_gate_fwd(x, k, v, wh, we, out, gate)
+            eg.tk_engram_gate_bwd(gout, x, k, v, wh, we, dx, dk, dv, ws)
+            eg.tk_engram_grad_w_reduce(ws, P, H, wh, we, dwh, dwe)
+        else:
+            eg.tk_engram_gate_fwd_fused(x, k, v, w, out, gate)
+            eg.tk_engram_gate_bwd_reduce_noalloc(gout, x, k, v, wh, we, dx, dk, dv, dwh, dwe)
 
     step()
     torch.cuda.synchronize()

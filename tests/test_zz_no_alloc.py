@@ -65,7 +65,8 @@ def check_against_workspace_path(eg, dev, T, H, seed):
 
 
 @pytest.mark.parametrize("shapes", [
-    [(4099, 7168), (1000, 7168)],          # the tuned width, ragged, then fewer rows
+    [(20003, 7168), (4099, 7168), (1000, 7168)],   # the tuned width: two launches (epochs),
+                                                   # then one, ragged, then fewer rows
     [(3000, 2048), (700, 4096), (33, 256)],  # most partials (P = 512 at H = 2048), then
                                              # other widths over the leftovers
 ])
