@@ -413,11 +413,13 @@ __global__ __launch_bounds__(W * kWave) void gate_fwd_kernel(
   const int64_t step = walk.row_step;
   auto row = [&](int64_t i) { return first + (i < n ? i : n - 1) * step; };
 
+  // The weights are loaded before the first rows: loads complete in order,
+  // so the first row's dot product then waits for them alone.
+  WeightsReg<C> w64;
+  load_weights<NT, C, FULL, FUSED>(wts, tid, nchunk, w64.w);
   FwdBuf<C> buf[D];
 #pragma unroll
   for (int s = 0; s + 1 < D; ++s) fwd_load<NT, C, FULL>(buf[s], x, k, v, row(s), nchunk, tid);
-  WeightsReg<C> w64;
-  load_weights<NT, C, FULL, FUSED>(wts, tid, nchunk, w64.w);
 
   for (int64_t i = 0;; i += D) {
 #pragma unroll
@@ -581,12 +583,13 @@ __global__ __launch_bounds__(W * kWave) void gate_bwd_kernel(
   if (n > 0) {
     const int64_t step = walk.row_step;
     auto row = [&](int64_t i) { return first + (i < n ? i : n - 1) * step; };
+    // weights before the first rows (loads complete in order)
+    double w64[C][8];
+    load_weights<NT, C, FULL, FUSED>(wts, tid, nchunk, w64);
     BwdBuf<C> buf[D];
 #pragma unroll
     for (int s = 0; s + 1 < D; ++s)
       bwd_load<NT, C, FULL>(buf[s], gout, x, k, v, row(s), nchunk, tid);
-    double w64[C][8];
-    load_weights<NT, C, FULL, FUSED>(wts, tid, nchunk, w64);
     auto walk_rows = [&](const auto& wts) {
       for (int64_t i = 0;; i += D) {
 #pragma unroll
