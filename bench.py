@@ -605,6 +605,67 @@ def trace_summary(trace_csv: str, stats_csv: str, cmd: str) -> str:
     return "\n".join(out) + "\n"
 
 
+def widths_trace_summary(trace_csv: str, widths_jsonl: str, cmd: str) -> str:
+    """Markdown summary of a rocprofv3 kernel trace of `bench.py --widths`:
+    per width, the forward's and the backward's average per call (the sum of
+    a call's epoch launches), its fraction of 8 TB/s, and the HIP-event
+    figure the same run printed. Each width's plan is its own kernel
+    instantiation, in WIDTHS order."""
+    import csv
+    widths = [json.loads(line) for line in open(widths_jsonl) if line.startswith("{")]
+    rows = sorted(csv.DictReader(open(trace_csv)), key=lambda r: int(r["Start_Timestamp"]))
+    per = {}
+    for r in rows:
+        lab = _kernel_label(r["Kernel_Name"])
+        if lab.startswith(("gate_fwd_kernel", "gate_bwd_kernel")):
+            per.setdefault(lab, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    fwd_labels = [k for k in per if k.startswith("gate_fwd")]
+    bwd_labels = [k for k in per if k.startswith("gate_bwd")]
+    out = ["# Gate kernels at every planned width: rocprofv3 kernel trace", "",
+           "Command (from the repository root, on one MI355X):", "", "    " + cmd, "",
+           f"Summarised by `python3 bench.py --widths-trace-from {os.path.basename(trace_csv)} "
+           "<the run's stdout>` (paths of the run's output).", "",
+           "`bench.py --widths` runs the forward and then the backward 31 times each (one "
+           "untimed call, then 30 back to back) at each width, on about 470 MB per bf16 "
+           "tensor (T = 235 Mi / H), past the 256 MB Infinity Cache. A call is one or more "
+           "launches (epochs of about 240 MB per tensor); the averages are per call. "
+           "Fractions are algorithmic bytes (forward 8·T·H + 4·T + 8·H, backward "
+           "14·T·H + 8·H) over the trace's average per call, against 8 TB/s.", "",
+           f"Kernel source sha256 prefix: {kernel_source_hash()}.", "",
+           "| H | T | kernel | launches per call | calls | trace average per call (us) | "
+           "fraction of 8 TB/s | events in the same run (us) |",
+           "|---|---|---|---|---|---|---|---|"]
+    for w in widths:
+        T, H = w["T"], w["H"]
+        L = gate_launches(T, H)
+        ab = algorithmic_bytes(T, H)
+        for key, labels, ev in (("gate_fwd_kernel", fwd_labels, w["fwd_us"]),
+                                ("gate_bwd_kernel", bwd_labels, w["bwd_us"])):
+            n = L[key]
+            # the width's instantiation: the one whose dispatch count is 31 calls
+            cand = [k for k in labels if len(per[k]) == 31 * n and not k.endswith(", true>")]
+            lab = None
+            for k in cand:
+                avg = sum(per[k]) / (len(per[k]) / n) / 1e3
+                if abs(avg - ev) / ev < 0.1:
+                    lab = k
+                    break
+            if lab is None:
+                out.append(f"| {H} | {T} | `{key}` | {n} | (not found) | | | {ev:.1f} |")
+                continue
+            labels.remove(lab)
+            calls = len(per[lab]) // n
+            avg = sum(per[lab]) / calls / 1e3
+            b = ab["fwd" if key == "gate_fwd_kernel" else "bwd"]
+            out.append(f"| {H} | {T} | `{lab}` | {n} | {calls} | {avg:.1f} | "
+                       f"{b / (avg * 1e3) / HBM_PEAK_GBPS:.3f} | {ev:.1f} |")
+    out += ["", "Template arguments are <waves per row, chunks per thread, full rows, rows in "
+            "flight[, fp64 weights in LDS], fused weight>. H = 8192 runs the generic plan "
+            "(8 waves x 2 chunks, compiled with the tail mask, which is never taken at this "
+            "width)."]
+    return "\n".join(out) + "\n"
+
+
 def time_graph_step(eg, dev, T: int = 1024, H: int = 4096, reps: int = 50) -> dict:
     """One step (forward, backward, reduction) on a short batch, called eagerly
     through the Python binding and replayed from a captured HIP graph; the
@@ -1123,6 +1184,9 @@ def main():
                     help="suffix of the --footprint-from record's file name")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="summarise two rocprofv3 --pmc runs instead of benchmarking")
+    ap.add_argument("--widths-trace-from", nargs=2, metavar=("TRACE_CSV", "WIDTHS_JSONL"),
+                    help="summarise a rocprofv3 --kernel-trace run of --widths (and its "
+                         "stdout) into profiles/gate_kernels_widths_h2048_to_h8192_kernel_trace.md")
     ap.add_argument("--trace-from", nargs=2, metavar=("TRACE_CSV", "STATS_CSV"),
                     help="summarise a rocprofv3 --kernel-trace --stats run of the default "
                          "bench into profiles/engram_kernels_bench_default_kernel_trace.md")
@@ -1136,6 +1200,15 @@ def main():
     if args.memory_read_traffic_from:
         rec = memory_read_traffic(*args.memory_read_traffic_from)
         print(json.dumps(rec, indent=1, sort_keys=True))
+        return
+    if args.widths_trace_from:
+        cmd = ("rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_widths "
+               "-o widths -- python3 bench.py --widths > gpurun_out/widths.jsonl")
+        text = widths_trace_summary(args.widths_trace_from[0], args.widths_trace_from[1], cmd)
+        with open(os.path.join(PROFILES, "gate_kernels_widths_h2048_to_h8192_kernel_trace.md"),
+                  "w") as f:
+            f.write(text)
+        print(text)
         return
     if args.trace_from:
         cmd = ("rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof -o bench "

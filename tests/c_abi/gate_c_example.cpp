@@ -7,6 +7,9 @@
 //          gate = sigmoid(0) = 1/2 exactly and out = bf16(x + v / 2)
 //   all rows: gate in (0, 1); dv = bf16(gate * grad_out) bit for bit
 //   reruns: dwh and dwe bit-identical
+//   the fused-weight forward and backward (w = wh * we from
+//   tk_engram_fused_weight) and the allocation-free backward + reduction:
+//   the plain calls' outputs bit for bit
 // Exits 0 and prints "c abi example ok" on success.
 
 #include <hip/hip_runtime_api.h>
@@ -139,6 +142,50 @@ int main() {
     std::printf("weight gradients differ between reruns\n");
     return 1;
   }
+
+  // the same step through the fused weight and through the allocation-free
+  // backward, into fresh outputs: every byte must match the plain calls
+  double* dw;
+  uint16_t *fout, *fdx, *fdk, *fdv, *ndx, *ndk, *ndv;
+  float *fgate, *fws, *ndwh, *ndwe;
+  HIP_OK(hipMalloc(&dw, H * 8));
+  HIP_OK(hipMalloc(&fout, n * 2));
+  HIP_OK(hipMalloc(&fdx, n * 2));
+  HIP_OK(hipMalloc(&fdk, n * 2));
+  HIP_OK(hipMalloc(&fdv, n * 2));
+  HIP_OK(hipMalloc(&ndx, n * 2));
+  HIP_OK(hipMalloc(&ndk, n * 2));
+  HIP_OK(hipMalloc(&ndv, n * 2));
+  HIP_OK(hipMalloc(&fgate, T * 4));
+  HIP_OK(hipMalloc(&fws, ws_bytes));
+  HIP_OK(hipMalloc(&ndwh, H * 4));
+  HIP_OK(hipMalloc(&ndwe, H * 4));
+  TK_OK(tk_engram_fused_weight(dwh_, dwe_, dw, H, st));
+  TK_OK(tk_engram_gate_fwd_fused(dx_, dk_, dv_, dw, fout, fgate, T, H, 1e-6, st));
+  TK_OK(tk_engram_gate_bwd_fused(dgo, dx_, dk_, dv_, dw, fdx, fdk, fdv, fws, ws_bytes, T, H, 1e-6,
+                                 1e-4, st));
+  TK_OK(tk_engram_gate_bwd_reduce_noalloc(dgo, dx_, dk_, dv_, dwh_, dwe_, ndx, ndk, ndv, ndwh, ndwe,
+                                          T, H, 1e-6, 1e-4, st));
+  HIP_OK(hipStreamSynchronize(st));
+  struct Pair { const void* a; const void* b; size_t bytes; const char* name; };
+  const Pair pairs[] = {{dout, fout, n * 2, "fused out"}, {dgate, fgate, (size_t)T * 4, "fused gate"},
+                        {dxg, fdx, n * 2, "fused dx"},   {dkg, fdk, n * 2, "fused dk"},
+                        {dvg, fdv, n * 2, "fused dv"},   {dws, fws, ws_bytes, "fused partials"},
+                        {dxg, ndx, n * 2, "no-alloc dx"}, {dkg, ndk, n * 2, "no-alloc dk"},
+                        {dvg, ndv, n * 2, "no-alloc dv"}, {dgwh, ndwh, (size_t)H * 4, "no-alloc dwh"},
+                        {dgwe, ndwe, (size_t)H * 4, "no-alloc dwe"}};
+  for (const Pair& p : pairs) {
+    std::vector<uint8_t> ha(p.bytes), hb(p.bytes);
+    HIP_OK(hipMemcpy(ha.data(), p.a, p.bytes, hipMemcpyDeviceToHost));
+    HIP_OK(hipMemcpy(hb.data(), p.b, p.bytes, hipMemcpyDeviceToHost));
+    if (std::memcmp(ha.data(), hb.data(), p.bytes)) {
+      std::printf("%s differs from the plain calls\n", p.name);
+      return 1;
+    }
+  }
+  for (void* p : {(void*)dw, (void*)fout, (void*)fdx, (void*)fdk, (void*)fdv, (void*)ndx,
+                  (void*)ndk, (void*)ndv, (void*)fgate, (void*)fws, (void*)ndwh, (void*)ndwe})
+    HIP_OK(hipFree(p));
   HIP_OK(hipStreamDestroy(st));
   for (void* p : {(void*)dx_, (void*)dk_, (void*)dv_, (void*)dgo, (void*)dout, (void*)dxg,
                   (void*)dkg, (void*)dvg, (void*)dwh_, (void*)dwe_, (void*)dgate, (void*)dws,

@@ -56,6 +56,47 @@ int main() {
   EXPECT(tk_engram_gate_bwd(a, a, a, a, f, f, a, a, a, nullptr, 1 << 30, 4, 64, 1e-6, 1e-4,
                             nullptr),
          TK_ERR_NULL);
+  for (double clamp : {1e-39, 1e-300, 1e39})
+    EXPECT(tk_engram_gate_bwd(a, a, a, a, f, f, a, a, a, f, 1 << 30, 4, 64, 1e-6, clamp, nullptr),
+           TK_ERR_VALUE);
+
+  // the fused-weight forms: w (fp64) in place of wh and we
+  EXPECT(tk_engram_gate_fwd_fused(a, a, a, d, a, f, -1, 64, 1e-6, nullptr), TK_ERR_SHAPE);
+  EXPECT(tk_engram_gate_fwd_fused(a, a, a, nullptr, a, f, 4, 64, 1e-6, nullptr), TK_ERR_NULL);
+  EXPECT(tk_engram_gate_fwd_fused(a, a, a, d + 1, a, f, 4, 64, 1e-6, nullptr), TK_ERR_ALIGN);
+  EXPECT(tk_engram_gate_fwd_fused(nullptr, a, a, nullptr, a, f, 0, 64, 1e-6, nullptr), TK_SUCCESS);
+  EXPECT(tk_engram_gate_bwd_fused(a, a, a, a, d, a, a, a, f, 4, 4, 64, 1e-6, 1e-4, nullptr),
+         TK_ERR_WORKSPACE);
+  EXPECT(tk_engram_gate_bwd_fused(a, a, a, a, nullptr, a, a, a, f, 1 << 30, 4, 64, 1e-6, 1e-4,
+                                  nullptr),
+         TK_ERR_NULL);
+  EXPECT(tk_engram_gate_bwd_fused(a, a, a, a, d, a, a, a, f, 1 << 30, 4, 64, 1e-6, 0.0, nullptr),
+         TK_ERR_VALUE);
+
+  // the allocation-free backward: failing checks only (a passing call would launch)
+  EXPECT(tk_engram_gate_bwd_reduce_noalloc(a, a, a, a, f, f, a, a, a, f, f, -1, 64, 1e-6, 1e-4,
+                                           nullptr),
+         TK_ERR_SHAPE);
+  EXPECT(tk_engram_gate_bwd_reduce_noalloc(a, a, a, a, f, f, a, a, a, nullptr, f, 4, 64, 1e-6,
+                                           1e-4, nullptr),
+         TK_ERR_NULL);
+  EXPECT(tk_engram_gate_bwd_reduce_noalloc(a, a, a, a, f, f, a, a, a, f, f4, 4, 64, 1e-6, 1e-4,
+                                           nullptr),
+         TK_ERR_ALIGN);
+  EXPECT(tk_engram_gate_bwd_reduce_noalloc(a, a, a, a, f, f, a, a, a, f, f, 4, 64, 1e-6, 0.0,
+                                           nullptr),
+         TK_ERR_VALUE);
+
+  // launches per call: a pure function of (T, H), 0 exactly when there are no partials
+  for (int64_t T : Ts)
+    for (int64_t H : Hs)
+      for (int32_t b = 0; b < 2; ++b) {
+        const int64_t L = tk_engram_gate_launches(T, H, b);
+        if (L < 0 || (L == 0) != (tk_engram_num_partials(T, H) == 0)) return 1;
+      }
+
+  EXPECT(tk_engram_grad_w_reduce(f, TK_ENGRAM_MAX_PARTIALS + 1, 64, f, f, f, f, nullptr),
+         TK_ERR_UNSUPPORTED);
   EXPECT(tk_engram_grad_w_reduce(f, -1, 64, f, f, f, f, nullptr), TK_ERR_SHAPE);
   EXPECT(tk_engram_grad_w_reduce(f, 3, 64, f, f, f4, f, nullptr), TK_ERR_ALIGN);
   EXPECT(tk_engram_fused_weight(f, f, d, -1, nullptr), TK_ERR_SHAPE);
