@@ -277,7 +277,8 @@ __device__ __forceinline__ RowScalars row_gate(double sum_xx, double sum_kk,
 // flight. The buffers rotate by unrolling the row loop D times (no register
 // copies, which would make the compiler wait for the prefetch), and every
 // prefetch is issued unconditionally with its row index clamped to the
-// block's last row, so the final redundant loads re-read that row.
+// block's last row of the launch, so the final redundant loads re-read that
+// row (a branch around them measured slower).
 //
 // Cross-wave sums go through LDS slots indexed by row parity: a slot is
 // rewritten two rows later, after every thread has passed the barrier of
@@ -287,10 +288,11 @@ __device__ __forceinline__ RowScalars row_gate(double sum_xx, double sum_kk,
 // b, b + G, b + 2G, ... (row t belongs to block t mod G), which keeps the rows
 // in flight across the chip inside one sliding window of the tensors. A
 // launch covers iterations [iter0, iter0 + iters) of that walk: block b takes
-// rows b + (iter0 + i) G, i = 0 .. rows_of(b) - 1, never beyond T. A long
-// walk is split into several such launches (epochs): the blocks drift apart
-// as they go, widening the window of rows in flight, and each launch boundary
-// brings them back together.
+// rows b + (iter0 + i) G, i = 0 .. rows_of(first_row(b)) - 1, never beyond T.
+// A long walk is split into several such launches (epochs): on MI355X a
+// launch of many rows per block loses bandwidth as it goes, most plausibly
+// because the blocks drift apart and widen the window of rows in flight, and
+// each launch boundary brings them back in step.
 struct RowWalk {
   int64_t T;
   int64_t row_step;  // G
@@ -814,10 +816,10 @@ int64_t grid_of(const Plan& p, int64_t T) { return T < p.blocks ? T : p.blocks; 
 
 // Epochs: each launch of a walk covers at most about kEpochBytes of every
 // [T, H] tensor, i.e. at most that many bytes / (G * 2H) rows per block. On
-// MI355X a single launch of many rows per block loses bandwidth as the
-// blocks drift apart (the backward at H = 7168: 0.73 of 8 TB/s at 16384
-// rows, 0.70 at 65536 and 0.64 at 131072 in one launch; the same rows in
-// launches of 16384 keep 0.72-0.73 throughout).
+// MI355X a single launch of many rows per block loses bandwidth (the
+// backward at H = 7168: 0.73 of 8 TB/s at 16384 rows, 0.70 at 65536 and
+// 0.64 at 131072 in one launch; the same rows in launches of 16384 keep
+// 0.72-0.73 throughout). 240 MB measured best among 96 to 480 MB.
 constexpr int64_t kEpochBytes = (int64_t)240 << 20;
 
 int64_t epoch_iters(int64_t G, int64_t H) {
