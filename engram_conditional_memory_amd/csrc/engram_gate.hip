@@ -1176,8 +1176,10 @@ tk_status tk_engram_gate_bwd_reduce_noalloc(const uint16_t* grad_out, const uint
                                             double dsqrt_clamp, void* stream) {
   tk_status st = check_bwd_args(grad_out, x, k, v, wh, we, dx, dk, dv, T, H, eps, dsqrt_clamp);
   if (st != TK_SUCCESS) return st;
-  if (!dwh || !dwe) return TK_ERR_NULL;
-  if (!aligned16(dwh) || !aligned16(dwe)) return TK_ERR_ALIGN;
+  // the reduction reads wh and we and writes dwh and dwe even when T = 0
+  if (!wh || !we || !dwh || !dwe) return TK_ERR_NULL;
+  if (!aligned16(wh) || !aligned16(we) || !aligned16(dwh) || !aligned16(dwe))
+    return TK_ERR_ALIGN;
   if (tk_engram_bwd_workspace_bytes(T, H) > sizeof(scratch)) return TK_ERR_WORKSPACE;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   float* partial = nullptr;

@@ -193,7 +193,8 @@ tk_status tk_engram_grad_w_reduce(const float* workspace, int64_t P, int64_t H,
  * array, which keeps the last call's partials: the backward writes every
  * partial it uses, so nothing needs clearing, but calls that overlap on one
  * GPU (two streams in flight at once) race and must be serialised by the
- * caller. T = 0 writes zeros to dwh and dwe.
+ * caller. T = 0 writes zeros to dwh and dwe (wh, we, dwh and dwe are
+ * checked then too, since the reduction still runs).
  */
 #define TK_ENGRAM_NOALLOC_SCRATCH_BYTES (256u * 8192u * 4u)
 

@@ -86,6 +86,12 @@ int main() {
   EXPECT(tk_engram_gate_bwd_reduce_noalloc(a, a, a, a, f, f, a, a, a, f, f, 4, 64, 1e-6, 0.0,
                                            nullptr),
          TK_ERR_VALUE);
+  EXPECT(tk_engram_gate_bwd_reduce_noalloc(a, a, a, a, nullptr, f, a, a, a, f, f, 0, 64, 1e-6,
+                                           1e-4, nullptr),
+         TK_ERR_NULL);
+  EXPECT(tk_engram_gate_bwd_reduce_noalloc(a, a, a, a, f, f4, a, a, a, f, f, 0, 64, 1e-6, 1e-4,
+                                           nullptr),
+         TK_ERR_ALIGN);
 
   // launches per call: a pure function of (T, H), 0 exactly when there are no partials
   for (int64_t T : Ts)

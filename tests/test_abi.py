@@ -156,6 +156,11 @@ def test_noalloc_backward_argument_checks():
         assert noalloc(**{name: A4}) == B.TK_ERR_ALIGN, name
     assert noalloc(T=0, dwh=None) == B.TK_ERR_NULL
     assert noalloc(T=0, dwe=A4) == B.TK_ERR_ALIGN
+    # with T = 0 the reduction still runs (zeros into dwh, dwe) and reads the
+    # weights, so they are checked too
+    assert noalloc(T=0, wh=None) == B.TK_ERR_NULL
+    assert noalloc(T=0, we=None) == B.TK_ERR_NULL
+    assert noalloc(T=0, we=A4) == B.TK_ERR_ALIGN
 
 
 def test_reduce_argument_checks():
