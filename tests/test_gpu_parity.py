@@ -664,6 +664,36 @@ def test_other_widths_many_rows_per_block(eg, cuda_device, T, H):
     assert_dv_is_gate_times_grad(d, g)
 
 
+@pytest.mark.parametrize("H", [8, 256, 520, 1032, 2048, 2056, 3072, 4096, 4104, 5120, 6144, 7168,
+                               8192])
+def test_fused_and_noalloc_forms_at_every_plan(eg, cuda_device, H):
+    """Every width's launch plan has its own kernels, in a plain and a
+    fused-weight form: the fused-weight forward and backward, and the
+    allocation-free backward + reduction, must give the plain calls' outputs
+    bit for bit at each of them (planned widths, generic plans, masked tail
+    chunks)."""
+    import torch
+    dev = cuda_device
+    T = 600
+    d = make_case(T, H, seed=H + 5)
+    x, k, v, g = (to_dev(d[n], dev) for n in ("x", "k", "v", "grad_out"))
+    wh, we = torch.from_numpy(d["wh"]).to(dev), torch.from_numpy(d["we"]).to(dev)
+    out, gate = eg.tk_engram_gate_fwd(x, k, v, wh, we)
+    dx, dk, dv, ws, P = eg.tk_engram_gate_bwd(g, x, k, v, wh, we)
+    dwh, dwe = eg.tk_engram_grad_w_reduce(ws, P, H, wh, we)
+    w = eg.tk_engram_fused_weight(wh, we)
+    f_out, f_gate = eg.tk_engram_gate_fwd_fused(x, k, v, w)
+    f_dx, f_dk, f_dv, f_ws, _ = eg.tk_engram_gate_bwd_fused(g, x, k, v, w)
+    n_dx, n_dk, n_dv, n_dwh, n_dwe = eg.tk_engram_gate_bwd_reduce_noalloc(g, x, k, v, wh, we)
+    torch.cuda.synchronize()
+    for name, a, b in (("out", out, f_out), ("gate", gate, f_gate), ("dx", dx, f_dx),
+                       ("dk", dk, f_dk), ("dv", dv, f_dv), ("partials", ws, f_ws),
+                       ("noalloc dx", dx, n_dx), ("noalloc dk", dk, n_dk),
+                       ("noalloc dv", dv, n_dv), ("noalloc dwh", dwh, n_dwh),
+                       ("noalloc dwe", dwe, n_dwe)):
+        assert same_bits(a, b), f"{name} differs at H={H}"
+
+
 def test_nan_row_stays_in_its_row(eg, cuda_device):
     # rows are independent in the forward: a NaN in one token's hidden row
     # gives that token a NaN gate and output and leaves every other row as
