@@ -45,7 +45,7 @@ struct TableParams {
   uint64_t mult[kMaxN];  // multiplier of window position i; 0 for i >= N
   uint64_t recip;        // floor((2^64 - 1) / M)
   uint32_t mod;          // M
-  uint32_t unused;
+  uint32_t neg_r1m;      // -(floor(recip / 2^32) * M) mod 2^32
 };
 
 struct HashParams {
@@ -66,24 +66,32 @@ struct HashParams {
 // h = h1 2^32 + h0 and R = R1 2^32 + R0,
 //   q = h1 R1 + floor(A / 2^32),   A = h1 R0 + h0 R1 + floor(h0 R0 / 2^32),
 // and the bits of A above 64 only reach bits of q above 31, so A is summed
-// modulo 2^64. The subtraction uses min(r, r - m): below m, r - m wraps
-// above r.
-__device__ __forceinline__ uint32_t mod_exact(uint64_t h, uint64_t recip, uint32_t m) {
+// modulo 2^64. Then, modulo 2^32,
+//   r = h0 - q m = h0 + h1 c - floor(A / 2^32) m,   c = -(R1 m),
+// with c precomputed per table, so that h0 + h1 c is one 32 x 32 + 64-bit
+// multiply-add on h itself. The subtraction uses min(r, r - m): below m,
+// r - m wraps above r.
+__device__ __forceinline__ uint32_t mod_exact(uint64_t h, uint64_t recip, uint32_t m,
+                                              uint32_t neg_r1m) {
   const uint32_t h0 = (uint32_t)h, h1 = (uint32_t)(h >> 32);
   const uint32_t r0 = (uint32_t)recip, r1 = (uint32_t)(recip >> 32);
-  const uint64_t a = (uint64_t)h1 * r0 + __umulhi(h0, r0) + (uint64_t)h0 * r1;
-  const uint32_t q = h1 * r1 + (uint32_t)(a >> 32);
-  const uint32_t r = h0 - q * m;
+  const uint64_t a = (uint64_t)h0 * r1 + ((uint64_t)h1 * r0 + __umulhi(h0, r0));
+  const uint32_t r = h0 + h1 * neg_r1m - (uint32_t)(a >> 32) * m;
   return min(r, r - m);
 }
 
 template <int NMAX>
 __device__ __forceinline__ uint32_t table_index(const uint32_t (&tok)[NMAX],
                                                 const TableParams& t) {
+  // tok * mult mod 2^64 = tok * lo(mult) + (tok * hi(mult) mod 2^32) 2^32:
+  // written so, each product is one 32-bit multiply and one multiply-add
   uint64_t h = 0;
 #pragma unroll
-  for (int i = 0; i < NMAX; ++i) h ^= (uint64_t)tok[i] * t.mult[i];
-  return mod_exact(h, t.recip, t.mod);
+  for (int i = 0; i < NMAX; ++i) {
+    const uint32_t m0 = (uint32_t)t.mult[i], m1 = (uint32_t)(t.mult[i] >> 32);
+    h ^= (uint64_t)tok[i] * m0 + ((uint64_t)(tok[i] * m1) << 32);
+  }
+  return mod_exact(h, t.recip, t.mod, t.neg_r1m);
 }
 
 // tok[i] = token at position s - i of the sequence, `pad` before its start
@@ -221,6 +229,7 @@ extern "C" tk_status tk_engram_hash(const int32_t* tokens, int64_t B, int64_t S,
         p.t[q].mult[i] = i < ngram[l] ? mult[(int64_t)q * kMaxN + i] : 0;
       p.t[q].mod = table_size[q];
       p.t[q].recip = UINT64_MAX / table_size[q];
+      p.t[q].neg_r1m = 0u - (uint32_t)(p.t[q].recip >> 32) * table_size[q];
     }
   }
   const dim3 grid((unsigned)((S + kHashBlock - 1) / kHashBlock), (unsigned)B);
