@@ -548,7 +548,9 @@ def trace_summary(trace_csv: str, stats_csv: str, cmd: str) -> str:
            "Command (from the repository root, on one MI355X):", "", "    " + cmd, "",
            f"Summarised by `python3 bench.py --trace-from {os.path.basename(trace_csv)} "
            f"{os.path.basename(stats_csv)}` (paths of the run's output directory).", "",
-           TRACE_DOC, "", f"Kernel source sha256 prefix: {kernel_source_hash()}.", "",
+           TRACE_DOC, "",
+           f"Kernel source sha256 prefixes: gate {kernel_source_hash()}, "
+           f"hash {kernel_source_hash(HASH_SRC)}, gather {kernel_source_hash(GATHER_SRC)}.", "",
            "Per dispatch, from the stats file (durations in microseconds):", "",
            "| kernel | dispatches | average | min | max | % of GPU time |",
            "|---|---|---|---|---|---|"]

@@ -664,6 +664,20 @@ def test_other_widths_many_rows_per_block(eg, cuda_device, T, H):
     assert_dv_is_gate_times_grad(d, g)
 
 
+@pytest.mark.parametrize("T,H", [(61441, 2048), (49153, 3072), (24577, 5120), (20481, 6144),
+                                 (16385, 8192)])
+def test_other_widths_across_epochs(eg, cuda_device, T, H):
+    # the same plans at one row past the first epoch's last: each call runs
+    # as two launches, the second carrying each workgroup's weight-gradient
+    # sum on from the first, compared on every element
+    assert eg.tk_engram_gate_launches(T, H, 0) == 2
+    assert eg.tk_engram_gate_launches(T, H, 1) == 2
+    d = make_case(T, H, seed=T + H)
+    g = run_gpu(eg, d, cuda_device)
+    assert_report(compare(d, g), name=f"T={T} H={H}")
+    assert_dv_is_gate_times_grad(d, g)
+
+
 @pytest.mark.parametrize("H", [8, 256, 520, 1032, 2048, 2056, 3072, 4096, 4104, 5120, 6144, 7168,
                                8192])
 def test_fused_and_noalloc_forms_at_every_plan(eg, cuda_device, H):
