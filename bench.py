@@ -48,6 +48,8 @@ HASH_SRC = os.path.join(ROOT, "engram_conditional_memory_amd", "csrc", "engram_h
 # VALU instruction of a 64-wide wave every 4 cycles (16 lanes per cycle)
 VALU_WAVE_INSTS_PER_S = 256 * 4 * 2.4e9 / 4
 HASH_WORKLOAD = "hash_b1024s4096"
+# GPU time of untimed warm-up before a timed line that follows host-side work
+WARM_MS = 50.0
 GATHER_SRC = os.path.join(ROOT, "engram_conditional_memory_amd", "csrc", "engram_gather.hip")
 MEMORY_READ_TRAFFIC = "traffic_memory_read.json"
 
@@ -113,13 +115,29 @@ class Workload:
             setattr(self, n, None)
 
 
-def avg_launch_us(fn, reps: int) -> float:
+def avg_launch_us(fn, reps: int, min_warmup_ms: float = 0.0) -> float:
     """Average duration of one call of `fn`, from HIP events on the launch
     stream around `reps` back-to-back calls (the queue stays ahead of the
-    host, so the figure is the kernels' own time)."""
+    host, so the figure is the kernels' own time). One untimed call comes
+    first; with min_warmup_ms, untimed calls continue until that much GPU
+    time has passed, for calls that follow host-side work during which the
+    GPU idled (its first ~10 ms of work afterwards run slow)."""
     import torch
     fn()
     torch.cuda.synchronize()
+    if min_warmup_ms > 0:
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        n = 1
+        while True:
+            for _ in range(n):
+                fn()
+            b.record()
+            torch.cuda.synchronize()
+            if a.elapsed_time(b) >= min_warmup_ms:
+                break
+            n *= 2
     a = torch.cuda.Event(enable_timing=True)
     b = torch.cuda.Event(enable_timing=True)
     a.record()
@@ -179,11 +197,14 @@ def time_workload(w: Workload, steps: int, warmup: int, min_warmup_ms: float = 0
     }
 
 
-def time_autograd(w: Workload, eg, steps: int, warmup: int, raw_ms: float) -> dict:
+def time_autograd(w: Workload, eg, steps: int, warmup: int, raw_ms: float,
+                  min_warmup_ms: float = 50.0) -> dict:
     """The autograd wrapper (EngramGate) on a workload's tensors: forward, then
     backward with fresh .grad tensors each step (set to None first, as
     zero_grad(set_to_none=True) does); HIP events on torch's current stream.
-    The outputs and gradients come from torch's caching allocator."""
+    The outputs and gradients come from torch's caching allocator. Warm-up
+    runs `warmup` steps and at least min_warmup_ms of GPU time, as the
+    secondary workloads' does: the first ~10 ms of a phase run slow."""
     import torch
     layer = eg.EngramGate(w.H, device=w.x.device)
     with torch.no_grad():
@@ -197,11 +218,20 @@ def time_autograd(w: Workload, eg, steps: int, warmup: int, raw_ms: float) -> di
             t.grad = None
         layer(x, k, v).backward(w.g)
 
-    for _ in range(warmup):
-        step()
+    # the first step allocates the outputs; the warm-up clock starts after it
+    step()
     torch.cuda.synchronize()
     a = torch.cuda.Event(enable_timing=True)
     b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    done, elapsed = 1, 0.0
+    while done < warmup or elapsed < min_warmup_ms:
+        step()
+        done += 1
+        if done >= warmup:
+            b.record()
+            torch.cuda.synchronize()
+            elapsed = a.elapsed_time(b)
     a.record()
     for _ in range(steps):
         step()
@@ -211,7 +241,7 @@ def time_autograd(w: Workload, eg, steps: int, warmup: int, raw_ms: float) -> di
     for t in leaves:
         t.grad = None
     del layer, x, k, v, leaves
-    return {"workload": w.c.name, "steps": steps, "ms_per_step": ms,
+    return {"workload": w.c.name, "warmup_steps": done, "steps": steps, "ms_per_step": ms,
             "tokens_per_s": w.T / (ms / 1e3), "vs_c_abi_step": raw_ms / ms}
 
 
@@ -524,16 +554,17 @@ def _kernel_label(name: str) -> str:
 
 
 TRACE_DOC = """bench.py defaults: 50 timed steps after 20 warm-up steps, then each call alone
-50 times back to back (plus one untimed call), on T=32768 H=7168; then 23
-steps (3 warm-up) of the autograd module on the same tensors (it runs the
-fused-weight forms of the gate kernels, the last template argument `true`);
-the same calls on T=16384 H=4096 after at least 50 ms of warm-up steps; 20
-steps and 20 single calls on the stress workload (T=65537, H=7168) after at
-least 50 ms of warm-up; the 1024-token forward 51 times hot and 50 times after
-a 1 GiB write; the copy probe; the stream probe for the 3-in/1-out and
-4-in/3-out mixes; the N-gram hash; the table gather on uniform, then Zipf(1)
-token ids; the fused weight at H=7168; a 1024-token step at H=4096 eagerly,
-on the capture stream and replayed from a HIP graph."""
+50 times back to back (plus one untimed call), on T=32768 H=7168; then 20
+steps of the autograd module on the same tensors after at least 20 steps and
+50 ms of warm-up (it runs the fused-weight forms of the gate kernels, the
+last template argument `true`); the same calls on T=16384 H=4096 after at
+least 50 ms of warm-up steps; 20 steps and 20 single calls on the stress
+workload (T=65537, H=7168) after at least 50 ms of warm-up; the 1024-token
+forward 51 times hot and 50 times after a 1 GiB write; the copy probe; the
+stream probe for the 3-in/1-out and 4-in/3-out mixes; the N-gram hash; the
+table gather on uniform, then Zipf(1) token ids; the fused weight at H=7168;
+a 1024-token step at H=4096 eagerly, on the capture stream and replayed from
+a HIP graph."""
 
 
 def trace_summary(trace_csv: str, stats_csv: str, cmd: str) -> str:
@@ -725,7 +756,7 @@ def time_hash(eg, dev, name: str = "b1024s4096", reps: int = 20) -> dict:
     def call():
         eg.tk_engram_hash(tokens, p["ngram"], p["mult"], p["table_size"], p["pad"], out)
 
-    us = avg_launch_us(call, reps)
+    us = avg_launch_us(call, reps, min_warmup_ms=WARM_MS)
     n = c.B * c.S
     nbytes = n * (4 + 4 * len(c.ngram) * c.tables)
     del tokens, out
@@ -769,7 +800,7 @@ def time_gather(eg, dev, reps: int = 20) -> tuple:
         def call():
             eg.tk_engram_gather(idx2, data, off, sizes, out)
 
-        us = avg_launch_us(call, reps)
+        us = avg_launch_us(call, reps, min_warmup_ms=WARM_MS)
         ih = idx2.cpu().numpy()
         distinct = sum(len(np.unique(ih[:, q])) for q in range(gc.tables))
         n = gc.T * gc.tables
@@ -794,17 +825,8 @@ def copy_ceiling(nbytes: int, eg, dev, reps: int = 20) -> dict:
     import torch
     src = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=dev).fill_(1.0)
     dst = torch.empty_like(src)
-    for _ in range(3):
-        eg.tk_engram_copy_probe(src, dst)
-    torch.cuda.synchronize()
-    a = torch.cuda.Event(enable_timing=True)
-    b = torch.cuda.Event(enable_timing=True)
-    a.record()
-    for _ in range(reps):
-        eg.tk_engram_copy_probe(src, dst)
-    b.record()
-    torch.cuda.synchronize()
-    us = 1e3 * a.elapsed_time(b) / reps
+    us = avg_launch_us(lambda: eg.tk_engram_copy_probe(src, dst), reps,
+                       min_warmup_ms=WARM_MS)
     del src, dst
     torch.cuda.empty_cache()
     return {"bytes_moved": 2 * nbytes, "us": us, "GBps": 2 * nbytes / (us * 1e3),
@@ -819,7 +841,8 @@ def mix_ceiling(nsrc: int, ndst: int, nbytes: int, eg, dev, reps: int = 20) -> d
     srcs = [torch.randint(-(1 << 31), (1 << 31) - 1, (n,), dtype=torch.int32, device=dev)
             for _ in range(nsrc)]
     dsts = [torch.empty_like(srcs[0]) for _ in range(ndst)]
-    us = avg_launch_us(lambda: eg.tk_engram_stream_probe(srcs, dsts), reps)
+    us = avg_launch_us(lambda: eg.tk_engram_stream_probe(srcs, dsts), reps,
+                       min_warmup_ms=WARM_MS)
     moved = (nsrc + ndst) * nbytes
     del srcs, dsts
     torch.cuda.empty_cache()
@@ -842,7 +865,7 @@ def time_fwd_small(eg, dev, reps: int = 50) -> dict:
     out = torch.empty_like(x)
     gate = torch.empty((c.T,), dtype=torch.float32, device=dev)
     fwd = eg.bind_gate_fwd(x, k, v, wh, we, out, gate)
-    hot = avg_launch_us(fwd, reps)
+    hot = avg_launch_us(fwd, reps, min_warmup_ms=WARM_MS)
     scrub = torch.empty(1 << 29, dtype=torch.int16, device=dev)
     times = []
     for i in range(reps):
@@ -1077,8 +1100,9 @@ def _per_dispatch(path: str, counter: str) -> list:
 
 def memory_read_traffic(fetch_csv: str, write_csv: str) -> dict:
     """HBM bytes per launch of the hash (its 4,194,304-token launches) and of
-    the gather (the first 21 launches on uniform token ids, the next 21 on
-    Zipf(1) ids) from two rocprofv3 --pmc runs over --memory-read, each
+    the gather (the launches after the hash of the uniform token ids, then
+    those after the hash of the Zipf(1) ids; each group's warm-up and timed
+    launches alike) from two rocprofv3 --pmc runs over --memory-read, each
     counter scaled by its reading for the copy probe of known size; written
     beside the profiles with the two kernel sources' sha256 prefixes."""
     import synth
@@ -1096,11 +1120,17 @@ def memory_read_traffic(fetch_csv: str, write_csv: str) -> dict:
         scale = copy_bytes / (1024.0 * float(np.mean(cp)))
         rec["calibration"][f"{counter.lower()}_scale"] = scale
         hash_v = [v for _, k, g, v in rows if k == "hash_kernel_vec" and g == hc.B * hc.S]
-        gat_v = [v for _, k, _, v in rows if k == "gather_kernel"]
-        if len(gat_v) != 42 or not hash_v:
-            raise SystemExit(f"{path}: expected 42 gather launches and the hash's, "
-                             f"found {len(gat_v)} and {len(hash_v)}")
-        for name, vals in (("hash", hash_v), ("gather", gat_v[:21]), ("gather_zipf", gat_v[21:])):
+        # the gather's index hashes (32768 tokens each) split its launches
+        groups = []
+        for _, k, g, v in rows:
+            if k == "hash_kernel_vec" and g == gc.T:
+                groups.append([])
+            elif k == "gather_kernel" and groups:
+                groups[-1].append(v)
+        if len(groups) != 2 or not all(groups) or not hash_v:
+            raise SystemExit(f"{path}: expected the hash's launches and two groups of gather "
+                             f"launches, found {len(hash_v)} and {[len(g) for g in groups]}")
+        for name, vals in (("hash", hash_v), ("gather", groups[0]), ("gather_zipf", groups[1])):
             per.setdefault(name, {})[key] = float(np.mean(vals)) * 1024.0 * scale
     algo = {"hash": hc.B * hc.S * (4 + 4 * len(hc.ngram) * hc.tables),
             "gather": gc.T * gc.tables * (4 + 4 * gc.d)}
@@ -1274,7 +1304,8 @@ def main():
     autograd_res = None
     if not args.no_secondary:
         print("[bench] timing the autograd wrapper", file=sys.stderr, flush=True)
-        autograd_res = time_autograd(w, eg, min(args.steps, 20), 3, main_res["ms_per_step"])
+        autograd_res = time_autograd(w, eg, min(args.steps, 20), args.warmup,
+                                     main_res["ms_per_step"])
     host = w.host
     w.free()
     torch.cuda.empty_cache()

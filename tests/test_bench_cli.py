@@ -110,10 +110,13 @@ def test_memory_read_traffic_splits_hash_and_gather(tmp_path, monkeypatch):
     for counter, scale in (("FETCH_SIZE", 2.0), ("WRITE_SIZE", 1.0)):
         rows = [(cp, 4194304, copy_bytes / scale / 1024)]
         rows += [(hk, h_tok, (4 * h_tok if counter == "FETCH_SIZE" else 64 * h_tok) / scale / 1024)] * 3
-        rows += [(hk, 32768, 1.0)]            # the gather's own small hash: ignored
         half = g_algo / 2
-        rows += [(gk, 8388608, half / scale / 1024)] * 21
-        rows += [(gk, 8388608, 0.9 * half / scale / 1024)] * 21
+        # each gather group follows the small hash of its own indices, and
+        # its warm-up makes the group's length vary
+        rows += [(hk, 32768, 1.0)]
+        rows += [(gk, 8388608, half / scale / 1024)] * 37
+        rows += [(hk, 32768, 1.0)]
+        rows += [(gk, 8388608, 0.9 * half / scale / 1024)] * 29
         with open(tmp_path / f"{counter}.csv", "w", newline="") as f:
             w = csv.DictWriter(f, fieldnames=fields)
             w.writeheader()
