@@ -667,9 +667,10 @@ def test_other_widths_many_rows_per_block(eg, cuda_device, T, H):
 @pytest.mark.parametrize("T,H", [(61441, 2048), (49153, 3072), (24577, 5120), (20481, 6144),
                                  (16385, 8192)])
 def test_other_widths_across_epochs(eg, cuda_device, T, H):
-    # the same plans at one row past the first epoch's last: each call runs
-    # as two launches, the second carrying each workgroup's weight-gradient
-    # sum on from the first, compared on every element
+    # the same plans past what one launch covers (by a single row at 2048,
+    # 5120 and 6144): each call runs as two launches, the second carrying
+    # each workgroup's weight-gradient sum on from the first, compared on
+    # every element
     assert eg.tk_engram_gate_launches(T, H, 0) == 2
     assert eg.tk_engram_gate_launches(T, H, 1) == 2
     d = make_case(T, H, seed=T + H)
