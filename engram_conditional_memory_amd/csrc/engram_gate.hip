@@ -785,7 +785,10 @@ tk_status check_shape(int64_t T, int64_t H) {
   return TK_SUCCESS;
 }
 
-bool finite_positive(double a) { return std::isfinite(a) && a > 0.0; }
+// RMSNorm epsilon: finite and at least 2^-126. The backward forms the
+// normalised rows r x in fp32, with r = 1/sqrt(mean(x^2) + eps); this bound
+// keeps r <= 2^63, so an all-zero row stays zero there (not inf * 0).
+bool eps_in_range(double a) { return std::isfinite(a) && a >= 0x1p-126; }
 
 // The derivative clamp is applied in fp32: it must round to a normal fp32.
 bool fp32_normal(double a) {
@@ -956,7 +959,7 @@ tk_status check_fwd_args(const uint16_t* x, const uint16_t* k, const uint16_t* v
                          const float* gate, int64_t T, int64_t H, double eps) {
   tk_status st = check_shape(T, H);
   if (st != TK_SUCCESS) return st;
-  if (!finite_positive(eps)) return TK_ERR_VALUE;
+  if (!eps_in_range(eps)) return TK_ERR_VALUE;
   if (T == 0) return TK_SUCCESS;
   if (!x || !k || !v || !w1 || !w2 || !out || !gate) return TK_ERR_NULL;
   if (!aligned16(x) || !aligned16(k) || !aligned16(v) || !aligned16(w1) ||
@@ -1005,7 +1008,7 @@ tk_status check_bwd_args(const uint16_t* grad_out, const uint16_t* x, const uint
                          int64_t T, int64_t H, double eps, double dsqrt_clamp) {
   tk_status st = check_shape(T, H);
   if (st != TK_SUCCESS) return st;
-  if (!finite_positive(eps) || !fp32_normal(dsqrt_clamp)) return TK_ERR_VALUE;
+  if (!eps_in_range(eps) || !fp32_normal(dsqrt_clamp)) return TK_ERR_VALUE;
   if (T == 0) return TK_SUCCESS;
   if (!grad_out || !x || !k || !v || !wh || !we || !dx || !dk || !dv) return TK_ERR_NULL;
   if (!aligned16(grad_out) || !aligned16(x) || !aligned16(k) || !aligned16(v) ||

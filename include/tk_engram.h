@@ -93,7 +93,10 @@ enum {
  *   wh, we  : fp32 [H]     RMSNorm weights of x and of k
  *   out     : bf16 [T, H]  out = x + gate * v
  *   gate    : fp32 [T]     the gate of each token
- *   eps     : RMSNorm epsilon (inside the square root), finite and > 0
+ *   eps     : RMSNorm epsilon (inside the square root), finite and at least
+ *             2^-126 (FLT_MIN), else TK_ERR_VALUE: the backward forms the
+ *             normalised rows 1/sqrt(mean + eps) * x in fp32, and the bound
+ *             keeps that scale finite (at most 2^63) for all-zero rows
  */
 tk_status tk_engram_gate_fwd(const uint16_t* x, const uint16_t* k,
                              const uint16_t* v, const float* wh,

@@ -45,6 +45,8 @@ int main() {
   EXPECT(tk_engram_gate_fwd(a, a, a, f, f, a, f, 4, 12, 1e-6, nullptr), TK_ERR_ALIGN);
   EXPECT(tk_engram_gate_fwd(a, a, a, f, f, a, f, 4, 8200, 1e-6, nullptr), TK_ERR_UNSUPPORTED);
   EXPECT(tk_engram_gate_fwd(a, a, a, f, f, a, f, 4, 64, 0.0, nullptr), TK_ERR_VALUE);
+  EXPECT(tk_engram_gate_fwd(a, a, a, f, f, a, f, 4, 64, 1e-39, nullptr), TK_ERR_VALUE);
+  EXPECT(tk_engram_gate_fwd(nullptr, a, a, f, f, a, f, 0, 64, 0x1p-126, nullptr), TK_SUCCESS);
   EXPECT(tk_engram_gate_fwd(nullptr, a, a, f, f, a, f, 0, 64, 1e-6, nullptr), TK_SUCCESS);
   EXPECT(tk_engram_gate_fwd(a, nullptr, a, f, f, a, f, 4, 64, 1e-6, nullptr), TK_ERR_NULL);
   EXPECT(tk_engram_gate_fwd(a, a, a, f4, f, a, f, 4, 64, 1e-6, nullptr), TK_ERR_ALIGN);

@@ -117,6 +117,14 @@ def test_forward_argument_checks():
     assert fwd(H=8200) == B.TK_ERR_UNSUPPORTED
     assert fwd(eps=0.0) == B.TK_ERR_VALUE
     assert fwd(eps=float("nan")) == B.TK_ERR_VALUE
+    # eps below 2^-126 would let the backward's fp32 row scale overflow
+    for eps in (1e-39, 2.0 ** -127, 1e-300, 5e-324, float("inf")):
+        assert fwd(eps=eps) == B.TK_ERR_VALUE, eps
+        assert fwd(eps=eps, T=0) == B.TK_ERR_VALUE, eps
+        assert bwd(eps=eps, T=0, ws=None, wsb=0) == B.TK_ERR_VALUE, eps
+        assert noalloc(eps=eps) == B.TK_ERR_VALUE, eps
+    assert fwd(eps=2.0 ** -126, T=0) == B.TK_SUCCESS
+    assert bwd(eps=2.0 ** -126, T=0, ws=None, wsb=0) == B.TK_SUCCESS
     assert fwd(T=0, x=None) == B.TK_SUCCESS          # empty: nothing to do
     for name in ("x", "k", "v", "wh", "we", "out", "gate"):
         assert fwd(**{name: None}) == B.TK_ERR_NULL, name

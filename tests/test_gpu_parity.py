@@ -59,7 +59,7 @@ def same_bits(a, b):
     return torch.equal(a.view(view), b.view(view))
 
 
-def run_gpu(eg, d, dev, backward=True, rerun=False, fused=False):
+def run_gpu(eg, d, dev, backward=True, rerun=False, fused=False, eps=oracle.EPS):
     """Forward (+ backward + reduction) on the GPU; returns host arrays. With
     `rerun`, every call runs a second time into fresh outputs, and each
     output must equal the first run's bit for bit. With `fused`, the forward
@@ -72,11 +72,11 @@ def run_gpu(eg, d, dev, backward=True, rerun=False, fused=False):
     we = torch.from_numpy(d["we"]).to(dev)
     if fused:
         w = eg.tk_engram_fused_weight(wh, we)
-        fwd = lambda: eg.tk_engram_gate_fwd_fused(x, k, v, w)  # noqa: E731
-        bwd = lambda g: eg.tk_engram_gate_bwd_fused(g, x, k, v, w)  # noqa: E731
+        fwd = lambda: eg.tk_engram_gate_fwd_fused(x, k, v, w, eps=eps)  # noqa: E731
+        bwd = lambda g: eg.tk_engram_gate_bwd_fused(g, x, k, v, w, eps=eps)  # noqa: E731
     else:
-        fwd = lambda: eg.tk_engram_gate_fwd(x, k, v, wh, we)  # noqa: E731
-        bwd = lambda g: eg.tk_engram_gate_bwd(g, x, k, v, wh, we)  # noqa: E731
+        fwd = lambda: eg.tk_engram_gate_fwd(x, k, v, wh, we, eps=eps)  # noqa: E731
+        bwd = lambda g: eg.tk_engram_gate_bwd(g, x, k, v, wh, we, eps=eps)  # noqa: E731
     out, gate = fwd()
     if rerun:
         out2, gate2 = fwd()
@@ -125,7 +125,7 @@ def row_classes(d):
     return cls
 
 
-def compare(d, g, backward=True, chunk=2048):
+def compare(d, g, backward=True, chunk=2048, eps=oracle.EPS):
     """Stream the oracle over the rows and collect every statistic."""
     T, H = d["x"].shape
     cls = row_classes(d)
@@ -139,7 +139,7 @@ def compare(d, g, backward=True, chunk=2048):
         b = min(T, a + chunk)
         sl = slice(a, b)
         o_out, o_gate, o_z = oracle.fwd_bf16(d["x"][sl], d["k"][sl], d["v"][sl],
-                                             d["wh"], d["we"])
+                                             d["wh"], d["we"], eps=eps)
         gate_err = max(gate_err, float(np.max(np.abs(g["gate"][sl] - o_gate))))
         nz = np.abs(o_z[o_z != 0])
         if nz.size:
@@ -148,7 +148,8 @@ def compare(d, g, backward=True, chunk=2048):
         del o_out
         if backward:
             o_dx, o_dk, o_dv, p_wh, p_we, _ = oracle.bwd_bf16(
-                d["grad_out"][sl], d["x"][sl], d["k"][sl], d["v"][sl], d["wh"], d["we"])
+                d["grad_out"][sl], d["x"][sl], d["k"][sl], d["v"][sl], d["wh"], d["we"],
+                eps=eps)
             st["dx"].add(g["dx"][sl], o_dx, cls[sl])
             st["dk"].add(g["dk"][sl], o_dk, cls[sl])
             st["dv"].add(g["dv"][sl], o_dv, cls[sl])
@@ -373,6 +374,34 @@ def test_special_rows(eg, cuda_device):
     assert np.all(oracle.bf16_to_f64(g["dk"][3]) == 0)
     # mirrored gate: sigmoid(-s) = 1 - sigmoid(s)
     assert abs(gate[4] + gate[5] - 1.0) < 2e-6
+
+
+@pytest.mark.parametrize("H", [4096, 7168])
+def test_smallest_eps(eg, cuda_device, H):
+    # eps = 2^-126, the smallest the calls accept: rows of zeros and rows far
+    # below eps get a normalising scale near 2^63, which the backward's fp32
+    # elementwise work must hold without overflow (a zero row stays zero)
+    T = 16
+
+    def fill(d):
+        z = np.zeros(H, dtype=np.uint16)
+        d["x"][0] = z
+        d["k"][1] = z
+        d["x"][2] = d["k"][2] = z
+        for t in (3, 4, 5):
+            d["x"][t] = synth.round_bf16(synth.bf16_to_f64(d["x"][t]) * 2.0 ** -120)
+        for t in (4, 6):
+            d["k"][t] = synth.round_bf16(synth.bf16_to_f64(d["k"][t]) * 2.0 ** -120)
+    d = make_case(T, H, seed=H + 126, fill=fill)
+    eps = 2.0 ** -126
+    g = run_gpu(eg, d, cuda_device, eps=eps)
+    assert_report(compare(d, g, eps=eps), name=f"eps 2^-126 H={H}")
+    for n in ("dx", "dk", "dv"):
+        assert np.all(np.isfinite(oracle.bf16_to_f64(g[n]))), n
+    assert np.all(np.isfinite(g["dwh"])) and np.all(np.isfinite(g["dwe"]))
+    # the row with x and k both zero: dx = grad_out and dk = 0 exactly
+    assert np.array_equal(g["dx"][2], d["grad_out"][2])
+    assert np.all(oracle.bf16_to_f64(g["dk"][2]) == 0)
 
 
 def test_derivative_clamp_region(eg, cuda_device):
