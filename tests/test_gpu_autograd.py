@@ -113,3 +113,36 @@ def test_frozen_weights_skip_the_reduction(eg, cuda_device):
     out.float().sum().backward()
     torch.cuda.synchronize()
     assert x.grad is not None and wh.grad is None and k.grad is None
+
+
+def test_module_at_the_main_workload_shape(eg, cuda_device):
+    """At 32768 tokens x 7168 (each call two launches), the shape the
+    autograd line of the benchmark times, the module's outputs and all five
+    gradients equal the C-ABI calls' bit for bit. The inputs are drawn on the
+    GPU; the C-ABI calls themselves are checked against the oracle at this
+    shape by the full-size parity tests."""
+    import torch
+    T, H = 32768, 7168
+    dev = cuda_device
+    g = torch.Generator(device=dev).manual_seed(32768)
+    x0, k0, v0, gout = (torch.randn((T, H), device=dev, generator=g).to(torch.bfloat16)
+                        for _ in range(4))
+    wh0 = 1 + 0.1 * torch.randn(H, device=dev, generator=g)
+    we0 = 1 + 0.1 * torch.randn(H, device=dev, generator=g)
+    m = eg.EngramGate(H, device=dev)
+    with torch.no_grad():
+        m.wh.copy_(wh0)
+        m.we.copy_(we0)
+    x, k, v = (t.clone().requires_grad_(True) for t in (x0, k0, v0))
+    out = m(x, k, v)
+    out.backward(gout)
+    o2, g2 = eg.tk_engram_gate_fwd(x0, k0, v0, wh0, we0)
+    dx, dk, dv, ws, P = eg.tk_engram_gate_bwd(gout, x0, k0, v0, wh0, we0)
+    dwh, dwe = eg.tk_engram_grad_w_reduce(ws, P, H, wh0, we0)
+    torch.cuda.synchronize()
+    assert eg.tk_engram_gate_launches(T, H, 1) == 2
+    assert torch.equal(out.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(m.last_gate, g2)
+    for a, b in ((x.grad, dx), (k.grad, dk), (v.grad, dv)):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    assert torch.equal(m.wh.grad, dwh) and torch.equal(m.we.grad, dwe)

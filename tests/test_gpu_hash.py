@@ -27,8 +27,9 @@ def gpu_hash(eg, dev, tokens, ngram, mult, table_size, pad):
     return out.cpu().numpy()
 
 
-@pytest.mark.parametrize("name", ["tiny", "b8s4096", "b8s4096_zipf", "b64s4096"])
+@pytest.mark.parametrize("name", ["tiny", "b8s4096", "b8s4096_zipf", "b64s4096", "b1024s4096"])
 def test_hash_workloads(eg, cuda_device, name):
+    # every index of every workload, the 4.2 M-token throughput one included
     c = synth.HASH_CONFIGS[name]
     p = synth.hash_params(c)
     t = synth.hash_tokens(c)
