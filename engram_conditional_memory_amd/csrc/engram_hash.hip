@@ -17,12 +17,17 @@
 // quotient q = mulhi64(h, floor((2^64 - 1) / M)), which is at most 1 below
 // floor(h / M), followed by one conditional subtraction in 32 bits.
 //
-// Every table runs the same number of products, NMAX (the largest N of any
-// layer), with the multipliers of positions i >= N set to 0 on the host: a
-// product with 0 leaves the XOR unchanged, so the result is the N-gram hash
-// of the table's own layer, and the kernel has no branches on N. Branching on
-// a table's N made each wave wait for that table's parameters from the
-// scalar cache before it could go on, which cost a third of the throughput.
+// The kernel has no branches on N. Branching on a table's N made each wave
+// wait for that table's parameters from the scalar cache before it could go
+// on, which cost a third of the throughput. Instead, each table's number of
+// products is fixed at compile time:
+//   - two layers of eight tables (the layout the pages describe) have an
+//     instance for every pair of orders (N0, N1), so a 2-gram table runs
+//     two products and a 3-gram table three;
+//   - every other layout runs NMAX products (the largest N of any layer) in
+//     every table, with the multipliers of positions i >= N set to 0 on the
+//     host: a product with 0 leaves the XOR unchanged, so the result is the
+//     N-gram hash of the table's own layer.
 
 #include <hip/hip_runtime.h>
 
@@ -54,6 +59,10 @@ struct HashParams {
   uint32_t pad;
 };
 
+// Layers of kPairK tables each, two of them: the layout with an instance per
+// pair of N-gram orders.
+constexpr int kPairK = 8;
+
 // h mod m for 1 <= m <= 2^31, with R = floor((2^64 - 1) / m).
 //
 // The quotient q = floor(h R / 2^64) is at most one below floor(h / m):
@@ -80,14 +89,17 @@ __device__ __forceinline__ uint32_t mod_exact(uint64_t h, uint64_t recip, uint32
   return min(r, r - m);
 }
 
-template <int NMAX>
+// The index of one table from its N products (N <= NMAX; the window holds
+// NMAX tokens).
+template <int NMAX, int N = NMAX>
 __device__ __forceinline__ uint32_t table_index(const uint32_t (&tok)[NMAX],
                                                 const TableParams& t) {
+  static_assert(N >= 1 && N <= NMAX, "a table uses at most the window's tokens");
   // tok * mult mod 2^64 = tok * lo(mult) + (tok * hi(mult) mod 2^32) 2^32:
   // written so, each product is one 32-bit multiply and one multiply-add
   uint64_t h = 0;
 #pragma unroll
-  for (int i = 0; i < NMAX; ++i) {
+  for (int i = 0; i < N; ++i) {
     const uint32_t m0 = (uint32_t)t.mult[i], m1 = (uint32_t)(t.mult[i] >> 32);
     h ^= (uint64_t)tok[i] * m0 + ((uint64_t)(tok[i] * m1) << 32);
   }
@@ -121,8 +133,10 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// L * K == LK, a multiple of 4: the output leaves in 16-byte stores.
-template <int LK, int NMAX>
+// L * K == LK, a multiple of 4: the output leaves in 16-byte stores. Tables
+// q < LK / 2 run N0 products and the others N1 (both NMAX unless the layout
+// is two layers of kPairK tables).
+template <int LK, int NMAX, int N0 = NMAX, int N1 = NMAX>
 __global__ __launch_bounds__(kHashBlock) void hash_kernel_vec(
     const int32_t* __restrict__ tokens, int64_t S, HashParams p,
     u32x4* __restrict__ out) {
@@ -139,7 +153,10 @@ __global__ __launch_bounds__(kHashBlock) void hash_kernel_vec(
   for (int q4 = 0; q4 < Q4; ++q4) {
     u32x4 v;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = table_index<NMAX>(tok, p.t[4 * q4 + e]);
+    for (int e = 0; e < 4; ++e) {
+      const int q = 4 * q4 + e;
+      v[e] = q < LK / 2 ? table_index<NMAX, N0>(tok, p.t[q]) : table_index<NMAX, N1>(tok, p.t[q]);
+    }
     ws[lane * Q4 + q4] = v;
   }
   wave_lds_sync();
@@ -173,17 +190,48 @@ __global__ __launch_bounds__(kHashBlock) void hash_kernel_any(
   for (int c = lane; c < ntok * LK; c += kWave) __builtin_nontemporal_store(ws[c], o + c);
 }
 
-template <int LK, int NMAX>
+template <int LK, int NMAX, int N0 = NMAX, int N1 = NMAX>
 hipError_t launch_vec(const int32_t* tokens, int64_t S, const HashParams& p, void* out,
                       dim3 grid, hipStream_t st) {
-  hipLaunchKernelGGL((hash_kernel_vec<LK, NMAX>), grid, dim3(kHashBlock), 0, st, tokens, S,
-                     p, reinterpret_cast<u32x4*>(out));
+  hipLaunchKernelGGL((hash_kernel_vec<LK, NMAX, N0, N1>), grid, dim3(kHashBlock), 0, st, tokens,
+                     S, p, reinterpret_cast<u32x4*>(out));
   return hipGetLastError();
 }
 
+// Two layers of kPairK tables whose orders differ: the instance for the pair
+// (n0, n1), max(n0, n1) == NMAX.
+template <int NMAX>
+hipError_t launch_pair(const int32_t* tokens, int64_t S, const HashParams& p, void* out,
+                       dim3 grid, hipStream_t st, int n0, int n1) {
+  constexpr int LK = 2 * kPairK;
+  const int lo = n0 < n1 ? n0 : n1;
+  const bool up = n0 < n1;  // the first layer has the lower order
+  switch (lo) {
+    case 1:
+      return up ? launch_vec<LK, NMAX, 1, NMAX>(tokens, S, p, out, grid, st)
+                : launch_vec<LK, NMAX, NMAX, 1>(tokens, S, p, out, grid, st);
+    case 2:
+      if constexpr (NMAX > 2)
+        return up ? launch_vec<LK, NMAX, 2, NMAX>(tokens, S, p, out, grid, st)
+                  : launch_vec<LK, NMAX, NMAX, 2>(tokens, S, p, out, grid, st);
+      break;
+    case 3:
+      if constexpr (NMAX > 3)
+        return up ? launch_vec<LK, NMAX, 3, NMAX>(tokens, S, p, out, grid, st)
+                  : launch_vec<LK, NMAX, NMAX, 3>(tokens, S, p, out, grid, st);
+      break;
+    default:
+      break;
+  }
+  return launch_vec<LK, NMAX>(tokens, S, p, out, grid, st);
+}
+
+// n0, n1: the orders of the two layers when the layout is two layers of
+// kPairK tables, else 0.
 template <int NMAX>
 hipError_t launch(const int32_t* tokens, int64_t S, const HashParams& p, void* out,
-                  dim3 grid, hipStream_t st) {
+                  dim3 grid, hipStream_t st, int n0, int n1) {
+  if (n0 > 0 && n0 != n1) return launch_pair<NMAX>(tokens, S, p, out, grid, st, n0, n1);
   switch (p.tables) {
     case 4: return launch_vec<4, NMAX>(tokens, S, p, out, grid, st);
     case 8: return launch_vec<8, NMAX>(tokens, S, p, out, grid, st);
@@ -232,14 +280,16 @@ extern "C" tk_status tk_engram_hash(const int32_t* tokens, int64_t B, int64_t S,
       p.t[q].neg_r1m = 0u - (uint32_t)(p.t[q].recip >> 32) * table_size[q];
     }
   }
+  const bool pair = L == 2 && K == kPairK;
+  const int n0 = pair ? ngram[0] : 0, n1 = pair ? ngram[1] : 0;
   const dim3 grid((unsigned)((S + kHashBlock - 1) / kHashBlock), (unsigned)B);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   hipError_t e;
   switch (nmax) {
-    case 1: e = launch<1>(tokens, S, p, out, grid, st); break;
-    case 2: e = launch<2>(tokens, S, p, out, grid, st); break;
-    case 3: e = launch<3>(tokens, S, p, out, grid, st); break;
-    default: e = launch<4>(tokens, S, p, out, grid, st); break;
+    case 1: e = launch<1>(tokens, S, p, out, grid, st, n0, n1); break;
+    case 2: e = launch<2>(tokens, S, p, out, grid, st, n0, n1); break;
+    case 3: e = launch<3>(tokens, S, p, out, grid, st, n0, n1); break;
+    default: e = launch<4>(tokens, S, p, out, grid, st, n0, n1); break;
   }
   return e == hipSuccess ? TK_SUCCESS : TK_ERR_LAUNCH;
 }

@@ -64,6 +64,26 @@ def test_hash_shapes_and_orders(eg, cuda_device, B, S, L, K, ngram):
         assert np.all(got[..., 0, 0] == 0)         # table of size 1
 
 
+@pytest.mark.parametrize("ngram", [(1, 2), (2, 1), (1, 3), (3, 1), (2, 3), (3, 2), (1, 4),
+                                   (4, 1), (2, 4), (4, 2), (3, 4), (4, 3), (3, 3)])
+def test_hash_two_layers_of_eight_tables(eg, cuda_device, ngram):
+    """Two layers of eight tables, the pages' layout, run an instance with
+    each layer's order fixed at compile time, one per ordered pair of
+    orders (and the shared one when both are equal): every pair, on a ragged
+    batch, bit-exact against the oracle."""
+    r = np.random.default_rng(1000 + 10 * ngram[0] + ngram[1])
+    B, S = 3, 777
+    tokens = r.integers(-(1 << 31), (1 << 31) - 1, size=(B, S), dtype=np.int64).astype(np.int32)
+    mult = r.integers(0, 1 << 63, size=(2, 8, 4), dtype=np.int64).astype(np.uint64)
+    mult = mult * np.uint64(2) + np.uint64(1)
+    sizes = r.integers(1, 1 << 31, size=(2, 8), dtype=np.int64).astype(np.uint32)
+    sizes[1, 7] = 1 << 31
+    pad = int(r.integers(0, 1 << 32))
+    want = oracle.engram_hash(tokens, ngram, mult, sizes, pad)
+    got = gpu_hash(eg, cuda_device, tokens, ngram, mult, sizes, pad)
+    assert np.array_equal(got, want)
+
+
 def test_hash_empty(eg, cuda_device):
     import torch
     c = synth.HASH_CONFIGS["tiny"]
