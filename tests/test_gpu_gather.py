@@ -109,6 +109,28 @@ def test_memory_read_full_size(eg, cuda_device, tokens_recipe):
         assert np.array_equal(got[sl], expected_rows(idx[sl], sizes, gc.d)), sl
 
 
+@pytest.mark.timeout(300)
+def test_gather_output_beyond_2_31_elements(eg, cuda_device):
+    """300000 tokens x 16 tables x 448 bf16: the output's 2.15e9 elements
+    pass the 32-bit range, so the offsets of the last tokens need 64 bits.
+    Indices are uniform over each table plus a few out of range; the first,
+    a middle and the last 4096 tokens are compared with the table pattern."""
+    import torch
+    T, Q, d = 300000, 16, 448
+    rows = np.full(Q, 1 << 19, dtype=np.uint32)
+    data, off = packed_tables(cuda_device, Q, rows, d)
+    r = np.random.default_rng(31)
+    idx = r.integers(-2, (1 << 19) + 2, size=(T, Q)).astype(np.int32)
+    out = eg.tk_engram_gather(torch.from_numpy(idx).to(cuda_device), data, off, rows)
+    torch.cuda.synchronize()
+    assert out.numel() > (1 << 31)
+    for a in (0, T // 2, T - 4096):
+        got = bits(out[a:a + 4096])
+        assert np.array_equal(got, expected_rows(idx[a:a + 4096], rows, d)), a
+    del out, data
+    torch.cuda.empty_cache()
+
+
 def test_memory_read_tiny_against_oracles(eg, cuda_device):
     import torch
     hc = synth.HASH_CONFIGS["tiny"]

@@ -135,3 +135,31 @@ def test_hash_modulus_at_its_edges(eg, cuda_device):
         assert [int(v) for v in row] == [t % int(M) for t, M in zip(targets, sizes)], call
         checked += K
     assert checked == 24 * 32
+
+
+@pytest.mark.timeout(300)
+def test_hash_output_beyond_2_31_elements(eg, cuda_device):
+    """One sequence of 2^27 + 1000 tokens: its 2 x 8 indices per token pass
+    the 32-bit element range (2^31 + 16000 of them, 8.6 GB), so the offsets
+    of the last waves need 64 bits. The first, a middle and the last 4096
+    positions are compared with the oracle, run on those positions and the
+    two tokens before them (the 3-gram window)."""
+    import torch
+    c = synth.HASH_CONFIGS["b8s4096"]
+    p = synth.hash_params(c)
+    S = (1 << 27) + 1000
+    r = np.random.default_rng(27)
+    tokens = r.integers(0, c.vocab, size=(1, S), dtype=np.int32)
+    t = torch.from_numpy(tokens).to(cuda_device)
+    out = eg.tk_engram_hash(t, p["ngram"], p["mult"], p["table_size"], p["pad"])
+    torch.cuda.synchronize()
+    assert out.numel() > (1 << 31)
+    back = max(p["ngram"]) - 1
+    for a in (0, S // 2, S - 4096):
+        lo = max(0, a - back)
+        want = oracle.engram_hash(tokens[:, lo:a + 4096], p["ngram"], p["mult"],
+                                  p["table_size"], p["pad"])[:, a - lo:]
+        got = out[:, a:a + 4096].cpu().numpy()
+        assert np.array_equal(got, want), a
+    del out, t
+    torch.cuda.empty_cache()
