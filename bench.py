@@ -561,10 +561,10 @@ last template argument `true`); the same calls on T=16384 H=4096 after at
 least 50 ms of warm-up steps; 20 steps and 20 single calls on the stress
 workload (T=65537, H=7168) after at least 50 ms of warm-up; the 1024-token
 forward 51 times hot and 50 times after a 1 GiB write; the copy probe; the
-stream probe for the 3-in/1-out and 4-in/3-out mixes; the N-gram hash; the
-table gather on uniform, then Zipf(1) token ids; the fused weight at H=7168;
-a 1024-token step at H=4096 eagerly, on the capture stream and replayed from
-a HIP graph."""
+stream probe for the 3-in/1-out and 4-in/3-out mixes; PyTorch's bf16 copy
+and addcmul on the same bytes; the N-gram hash; the table gather on uniform,
+then Zipf(1) token ids; the fused weight at H=7168; a 1024-token step at
+H=4096 eagerly, on the capture stream and replayed from a HIP graph."""
 
 
 def trace_summary(trace_csv: str, stats_csv: str, cmd: str) -> str:
@@ -848,6 +848,28 @@ def mix_ceiling(nsrc: int, ndst: int, nbytes: int, eg, dev, reps: int = 20) -> d
     torch.cuda.empty_cache()
     return {"reads": nsrc, "writes": ndst, "bytes_each": nbytes, "us": us,
             "GBps": moved / (us * 1e3), "frac": moved / (us * 1e3) / HBM_PEAK_GBPS}
+
+
+def vendor_reference(nbytes: int, dev, reps: int = 20) -> dict:
+    """PyTorch's own ROCm kernels on tensors of the same size, for reference
+    beside the library's probes: a bf16 copy (one read, one write) and
+    addcmul, out = x + k * v (three reads and one write, the forward's mix).
+    Random data, as for the probes."""
+    import torch
+    n = nbytes // 2
+    g = torch.Generator(device=dev).manual_seed(7)
+    x, k, v = (torch.randn(n, device=dev, generator=g).to(torch.bfloat16) for _ in range(3))
+    o = torch.empty_like(x)
+    res = {}
+    for name, fn, moved in (("torch_copy", lambda: o.copy_(x), 2 * nbytes),
+                            ("torch_addcmul_3r1w", lambda: torch.addcmul(x, k, v, out=o),
+                             4 * nbytes)):
+        us = avg_launch_us(fn, reps, min_warmup_ms=WARM_MS)
+        res[name] = {"us": us, "bytes": moved, "GBps": moved / (us * 1e3),
+                     "frac": moved / (us * 1e3) / HBM_PEAK_GBPS}
+    del x, k, v, o
+    torch.cuda.empty_cache()
+    return res
 
 
 def time_fwd_small(eg, dev, reps: int = 50) -> dict:
@@ -1340,6 +1362,7 @@ def main():
     main_res["fwd"]["frac_of_mix_ceiling"] = main_res["fwd"]["GBps"] / ceilings["fwd_3r1w"]["GBps"]
     main_res["bwd_kernel"]["frac_of_mix_ceiling"] = (main_res["bwd_kernel"]["GBps"]
                                                      / ceilings["bwd_4r3w"]["GBps"])
+    vendor = vendor_reference(tensor_bytes, dev)
     hash_res = gather_res = gather_zipf_res = fused_res = graph_res = None
     if not args.no_secondary:
         print("[bench] timing the N-gram hash", file=sys.stderr, flush=True)
@@ -1387,6 +1410,7 @@ def main():
         "fwd_small": small,
         "copy_probe": copy,
         "mix_ceilings": ceilings,
+        "vendor_reference": vendor,
         "hash": hash_res,
         "gather": gather_res,
         "autograd": autograd_res,
