@@ -342,6 +342,22 @@ def test_shapes(eg, cuda_device, T, H):
     assert_dv_is_gate_times_grad(d, g)
 
 
+def _random_shapes(n=30, seed=8192):
+    r = np.random.default_rng(seed)
+    return [(int(r.integers(1, 3001)), 8 * int(r.integers(1, 1025))) for _ in range(n)]
+
+
+@pytest.mark.parametrize("T,H", _random_shapes())
+def test_random_shapes(eg, cuda_device, T, H):
+    # seeded random widths (any multiple of 8 up to 8192, so mostly the
+    # generic plans with masked tail chunks) and token counts, every element
+    # against the oracle, the forward's gate reused bit for bit by dv
+    d = make_case(T, H, seed=T * 13 + H)
+    g = run_gpu(eg, d, cuda_device)
+    assert_report(compare(d, g), name=f"T={T} H={H}")
+    assert_dv_is_gate_times_grad(d, g)
+
+
 def test_special_rows(eg, cuda_device):
     T, H = 12, 4096
 
