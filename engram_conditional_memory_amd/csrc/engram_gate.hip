@@ -605,7 +605,9 @@ __global__ __launch_bounds__(W * kWave) void gate_bwd_kernel(
             // of the next row at the start of the iteration, grad_out and v
             // after this row's stores. Streams at equal offsets modulo 2 MiB
             // (separate allocations) then meet the same HBM banks less often;
-            // about 1% faster at H = 7168, every bit the same.
+            // about 1% faster at H = 7168, every bit the same. The plans with
+            // three rows in flight are the wide ones (5, 6 or 7 waves of two
+            // chunks per row); the two-wave plans run faster with two.
             const int64_t o = next * nchunk;
             load_row<NT, C, FULL>(x + o, tid, nchunk, nb.x);
             load_row<NT, C, FULL>(k + o, tid, nchunk, nb.k);
@@ -799,10 +801,10 @@ bool fp32_normal(double a) {
 // Launch plan for a row of nchunk 16-byte chunks: W waves per row, C chunks
 // per thread (FULL when W * 64 * C == nchunk, i.e. no masking), D rows in
 // flight per workgroup, weights in LDS (backward), and G workgroups walking
-// the rows interleaved (block b takes rows b, b + G, ...). The two tuned
-// widths have plans measured on MI355X; other widths take the fewest waves
-// that cover the row. G is also the backward's number of weight-gradient
-// partials, so it depends only on (T, H).
+// the rows interleaved (block b takes rows b, b + G, ...). The widths 2048,
+// 3072, 4096, 5120, 6144 and 7168 have plans measured on MI355X; other widths
+// take the fewest waves that cover the row. G is also the backward's number
+// of weight-gradient partials, so it depends only on (T, H).
 struct Plan {
   int W, C, D;
   bool full, wlds;
@@ -820,20 +822,20 @@ Plan generic_plan(int nchunk) {
 Plan fwd_plan(int nchunk) {
   if (nchunk == 896) return {7, 2, 2, true, false, 224};   // H = 7168
   if (nchunk == 512) return {2, 4, 3, true, false, 256};   // H = 4096
-  if (nchunk == 640) return {2, 5, 3, true, false, 256};   // H = 5120
+  if (nchunk == 640) return {5, 2, 2, true, false, 256};   // H = 5120
   if (nchunk == 384) return {3, 2, 3, true, false, 256};   // H = 3072
   if (nchunk == 256) return {1, 4, 2, true, false, 512};   // H = 2048
-  if (nchunk == 768) return {2, 6, 2, true, false, 256};   // H = 6144
+  if (nchunk == 768) return {6, 2, 2, true, false, 224};   // H = 6144
   return generic_plan(nchunk);
 }
 
 Plan bwd_plan(int nchunk) {
   if (nchunk == 896) return {7, 2, 3, true, true, 224};    // H = 7168
   if (nchunk == 512) return {2, 4, 2, true, false, 256};   // H = 4096
-  if (nchunk == 640) return {2, 5, 2, true, true, 256};    // H = 5120
+  if (nchunk == 640) return {5, 2, 3, true, true, 256};    // H = 5120
   if (nchunk == 384) return {3, 2, 2, true, false, 256};   // H = 3072
   if (nchunk == 256) return {1, 4, 2, true, false, 512};   // H = 2048
-  if (nchunk == 768) return {2, 6, 2, true, true, 256};    // H = 6144
+  if (nchunk == 768) return {6, 2, 3, true, true, 224};    // H = 6144
   return generic_plan(nchunk);
 }
 
@@ -880,10 +882,10 @@ template <bool F>
 tk_status dispatch_fwd(const Plan& p, const FwdArgs& a, int grid, hipStream_t st) {
   if (p.W == 7 && p.C == 2 && p.full && p.D == 2) return run_fwd<7, 2, true, 2, F>(a, grid, st);
   if (p.W == 2 && p.C == 4 && p.full && p.D == 3) return run_fwd<2, 4, true, 3, F>(a, grid, st);
-  if (p.W == 2 && p.C == 5 && p.full && p.D == 3) return run_fwd<2, 5, true, 3, F>(a, grid, st);
+  if (p.W == 5 && p.C == 2 && p.full && p.D == 2) return run_fwd<5, 2, true, 2, F>(a, grid, st);
   if (p.W == 3 && p.C == 2 && p.full && p.D == 3) return run_fwd<3, 2, true, 3, F>(a, grid, st);
   if (p.W == 1 && p.C == 4 && p.full && p.D == 2) return run_fwd<1, 4, true, 2, F>(a, grid, st);
-  if (p.W == 2 && p.C == 6 && p.full && p.D == 2) return run_fwd<2, 6, true, 2, F>(a, grid, st);
+  if (p.W == 6 && p.C == 2 && p.full && p.D == 2) return run_fwd<6, 2, true, 2, F>(a, grid, st);
   if (p.D == 2 && p.C == 1) {
     switch (p.W) {
       case 1: return run_fwd<1, 1, false, 2, F>(a, grid, st);
@@ -924,14 +926,14 @@ tk_status dispatch_bwd(const Plan& p, const BwdArgs& a, int grid, hipStream_t st
     return run_bwd<7, 2, true, 3, true, F>(a, grid, st);
   if (p.W == 2 && p.C == 4 && p.full && p.D == 2 && !p.wlds)
     return run_bwd<2, 4, true, 2, false, F>(a, grid, st);
-  if (p.W == 2 && p.C == 5 && p.full && p.D == 2 && p.wlds)
-    return run_bwd<2, 5, true, 2, true, F>(a, grid, st);
+  if (p.W == 5 && p.C == 2 && p.full && p.D == 3 && p.wlds)
+    return run_bwd<5, 2, true, 3, true, F>(a, grid, st);
   if (p.W == 3 && p.C == 2 && p.full && p.D == 2 && !p.wlds)
     return run_bwd<3, 2, true, 2, false, F>(a, grid, st);
   if (p.W == 1 && p.C == 4 && p.full && p.D == 2 && !p.wlds)
     return run_bwd<1, 4, true, 2, false, F>(a, grid, st);
-  if (p.W == 2 && p.C == 6 && p.full && p.D == 2 && p.wlds)
-    return run_bwd<2, 6, true, 2, true, F>(a, grid, st);
+  if (p.W == 6 && p.C == 2 && p.full && p.D == 3 && p.wlds)
+    return run_bwd<6, 2, true, 3, true, F>(a, grid, st);
   if (p.D == 2 && !p.wlds && p.C == 1) {
     switch (p.W) {
       case 1: return run_bwd<1, 1, false, 2, false, F>(a, grid, st);

@@ -699,10 +699,10 @@ def test_graph_capture_and_replay(eg, cuda_device, T, H, form):
                                  (6001, 6144)])
 def test_other_widths_many_rows_per_block(eg, cuda_device, T, H):
     # the plans of the other widths (H=2048: 1 wave x 4 chunks on 512
-    # workgroups; H=3072: 3 waves x 2 chunks; H=5120 and 6144: 2 waves x 5
-    # and x 6 chunks, weights in LDS in the backward; H=8192: 8 waves x 2
-    # chunks with the tail mask) with ~25-80 rows per workgroup, compared on
-    # every element
+    # workgroups; H=3072: 3 waves x 2 chunks; H=5120 and 6144: 5 and 6 waves
+    # x 2 chunks, the backward with three rows in flight and its weights in
+    # LDS; H=8192: 8 waves x 2 chunks with the tail mask) with ~25-80 rows
+    # per workgroup, compared on every element
     d = make_case(T, H, seed=T + H)
     g = run_gpu(eg, d, cuda_device)
     assert_report(compare(d, g), name=f"T={T} H={H}")
